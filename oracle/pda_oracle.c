@@ -1,0 +1,170 @@
+/*
+ * fp64 CPU oracle for paged grouped-query decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path calls this code: only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+ * shares no code, header or table with the GPU library.
+ *
+ * What it computes is the plain definition of single-token attention, written
+ * out directly -- two passes over each (sequence, q head)'s gathered token
+ * list -- with no online update, no splitting and no blocking:
+ *
+ *   score_t = (sum_d q[d] * K_t[d]) * (1 / sqrt(head_dim))
+ *   M = max_t score_t,  w_t = exp(score_t - M),  L = sum_t w_t,
+ *   O[d] = sum_t w_t * V_t[d],  out[d] = O[d] / L   (0 when L == 0)
+ *
+ * Sources (the pages that define the operation):
+ *  - AstrAI "CUDA Kernels" page, section "Python Wrappers": q/k/v are laid out
+ *    [batch, seq_len, n_heads, head_dim] and the scale is 1/sqrt(head_dim).
+ *  - spark_storage "tiled_attention.rs" page, file header comment: a running
+ *    (m, l, o) state, reset to (-inf, 0, 0), folded tile by tile, then o / l
+ *    stored as bf16.  (M, L, O) above is that state after every tile listed.
+ *  - same page, TiledAttention::paged_strides / scratch_pool_strides: the
+ *    (blk, tok, kvh) stride triple, in bf16 elements, addresses element d of
+ *    token slot j of kv head g in page b at b*blk + j*tok + g*kvh + d, for K
+ *    and for V alike.
+ *  - same page, TiledAttentionDims::validate and gqa_ratio: q heads are a
+ *    whole multiple of kv heads, their ratio G being passed to the kernel.
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *  - q head h reads kv head g = h / G (contiguous groups of G q heads).
+ *  - the last-valid count is given per sequence and per tile; it applies to the
+ *    last page that tile lists for the sequence, every other page being full.
+ *    Counts are clamped to [0, tile_capacity], last-valid counts to
+ *    [0, block_size].
+ *  - a sequence with no token gives M = -inf, L = 0, O = 0 and out = 0.
+ *  - the state's m is in natural-log units (the max of the scaled scores).
+ *
+ * Inputs are bf16 bit patterns; each is widened exactly to binary64 and all
+ * arithmetic is binary64.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static double bf16_to_f64(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi) {
+    return x < lo ? lo : (x > hi ? hi : x);
+}
+
+/*
+ * Element offsets (relative to a pool base) of every token row that sequence
+ * s lists for kv head g, in logical order: tile by tile, page by page, slot by
+ * slot.  Returns the number of rows, or -1 if a row would leave the pool.
+ */
+static int64_t gather_rows(int32_t s, int32_t g, int32_t num_seqs, int32_t block_size,
+                           int64_t blk, int64_t tok, int64_t kvh, int32_t head_dim,
+                           int32_t n_tiles, int32_t capacity, const int32_t *blocks,
+                           const int32_t *counts, const int32_t *last_valid,
+                           int64_t pool_rows_limit, int64_t *rows) {
+    int64_t n = 0;
+    for (int32_t t = 0; t < n_tiles; ++t) {
+        int32_t cnt = clamp_i32(counts[(int64_t)t * num_seqs + s], 0, capacity);
+        const int32_t *list = blocks + ((int64_t)t * num_seqs + s) * capacity;
+        for (int32_t i = 0; i < cnt; ++i) {
+            int32_t valid = block_size;
+            if (i == cnt - 1)
+                valid = clamp_i32(last_valid[(int64_t)t * num_seqs + s], 0, block_size);
+            for (int32_t j = 0; j < valid; ++j) {
+                int64_t r = (int64_t)list[i] * blk + (int64_t)j * tok + (int64_t)g * kvh;
+                if (list[i] < 0 || r < 0 || r + head_dim > pool_rows_limit) return -1;
+                rows[n++] = r;
+            }
+        }
+    }
+    return n;
+}
+
+/*
+ * Attention of one query token per sequence over the tokens listed by
+ * `n_tiles` tiles (the state after those tiles, and its finalised output).
+ *
+ *   q           bf16 [num_seqs, num_q_heads, head_dim]
+ *   pool        flat bf16 buffer of pool_elems elements; K rows start at
+ *               k_base, V rows at v_base, both addressed with (blk, tok, kvh)
+ *   blocks      int32 [n_tiles, num_seqs, capacity]
+ *   counts      int32 [n_tiles, num_seqs]
+ *   last_valid  int32 [n_tiles, num_seqs]
+ *   pairs       optional list of n_pairs indices s*num_q_heads + h to compute
+ *               (NULL: all num_seqs*num_q_heads, in order)
+ *   m, l        fp64 [n_pairs]; o, out fp64 [n_pairs, head_dim]
+ *
+ * Returns 0, or -1 on a page id or row outside the pool, -2 on bad
+ * dimensions, -3 on allocation failure.
+ */
+int pda_oracle_attend(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, const uint16_t *q,
+                      const uint16_t *pool, int64_t pool_elems, int64_t k_base, int64_t v_base,
+                      int64_t blk, int64_t tok, int64_t kvh, int32_t n_tiles, int32_t capacity,
+                      const int32_t *blocks, const int32_t *counts, const int32_t *last_valid,
+                      const int32_t *pairs, int64_t n_pairs, double *m, double *l, double *o,
+                      double *out, int nthreads) {
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        block_size <= 0 || n_tiles < 0 || capacity < 0 || num_q_heads % num_kv_heads != 0)
+        return -2;
+    if (pairs == NULL) n_pairs = (int64_t)num_seqs * num_q_heads;
+    const int32_t G = num_q_heads / num_kv_heads;
+    const double scale = 1.0 / sqrt((double)head_dim);
+    const int64_t max_rows = (int64_t)n_tiles * capacity * block_size;
+    const int64_t k_limit = pool_elems - k_base, v_limit = pool_elems - v_base;
+    const int64_t row_limit = k_limit < v_limit ? k_limit : v_limit;
+    int status = 0;
+    if (nthreads < 1) nthreads = 1;
+
+#pragma omp parallel num_threads(nthreads)
+    {
+        int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)(max_rows > 0 ? max_rows : 1));
+        double *score = (double *)malloc(sizeof(double) * (size_t)(max_rows > 0 ? max_rows : 1));
+        if (!rows || !score) {
+#pragma omp atomic write
+            status = -3;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < n_pairs; ++p) {
+            if (!rows || !score) continue;
+            const int64_t sh = pairs ? pairs[p] : p;
+            const int32_t s = (int32_t)(sh / num_q_heads), h = (int32_t)(sh % num_q_heads);
+            const int32_t g = h / G;
+            double *op = o + p * head_dim, *outp = out + p * head_dim;
+            int64_t n = gather_rows(s, g, num_seqs, block_size, blk, tok, kvh, head_dim, n_tiles,
+                                    capacity, blocks, counts, last_valid, row_limit, rows);
+            if (n < 0) {
+#pragma omp atomic write
+                status = -1;
+                continue;
+            }
+            const uint16_t *qh = q + ((int64_t)s * num_q_heads + h) * head_dim;
+            /* pass 1: scaled scores and their maximum */
+            double M = -INFINITY;
+            for (int64_t t = 0; t < n; ++t) {
+                const uint16_t *kr = pool + k_base + rows[t];
+                double acc = 0.0;
+                for (int32_t d = 0; d < head_dim; ++d) acc += bf16_to_f64(qh[d]) * bf16_to_f64(kr[d]);
+                score[t] = acc * scale;
+                if (score[t] > M) M = score[t];
+            }
+            /* pass 2: weights, their sum and the weighted sum of V rows */
+            double L = 0.0;
+            for (int32_t d = 0; d < head_dim; ++d) op[d] = 0.0;
+            for (int64_t t = 0; t < n; ++t) {
+                const uint16_t *vr = pool + v_base + rows[t];
+                double w = exp(score[t] - M);
+                L += w;
+                for (int32_t d = 0; d < head_dim; ++d) op[d] += w * bf16_to_f64(vr[d]);
+            }
+            m[p] = M;
+            l[p] = L;
+            for (int32_t d = 0; d < head_dim; ++d) outp[d] = L > 0.0 ? op[d] / L : 0.0;
+        }
+        free(rows);
+        free(score);
+    }
+    return status;
+}
