@@ -1,0 +1,147 @@
+"""Benchmark: paged GQA decode attention on one MI355X.
+
+One step is one pda_decode call (split-KV partial kernel + log-sum-exp combine
+kernel) over the ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
+head_dim 128, block_size 16, contexts log-uniform in [128, 32768], 1 % of keys
+scaled by 4, paged layout.  Inputs are seeded synthetic bf16, resident in HBM
+before the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+                    [--blocks-per-split N] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--blocks-per-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, min_seconds):
+    """The fp64 oracle as it stands, on the host cores, over the whole workload
+    (repeated until `min_seconds` have passed), in the metric's unit."""
+    import oracle
+    threads = oracle.host_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attend_workload(w, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per = el / reps
+    return {"value": w.algorithmic_bytes() / per / 1e12, "unit": "TB/s", "cores": threads,
+            "kind": "oracle", "us_per_call": per * 1e6,
+            "sample": f"whole workload ({w.num_seqs * w.num_q_heads} (sequence, q head) pairs), "
+                      f"{reps} repetition(s), fp64 C oracle with OpenMP"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    import workloads
+    import paged_gqa_decode_pda_amd as pda
+
+    log(f"generating workload {args.workload}")
+    w = workloads.config(args.workload)
+    if len(w.tiles) != 1:
+        raise SystemExit("the benchmark times the one-shot decode path; pick workload 1, 2 or 3")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b, c, v = w.stacked_tiles()
+    dims = pda.pda_dims(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                        w.tile_capacity)
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev)
+    pool = torch.from_numpy(w.pool.view(np.int16)).to(dev)
+    tables = torch.from_numpy(b[0]).to(dev)
+    counts = torch.from_numpy(c[0]).to(dev)
+    lastv = torch.from_numpy(v[0]).to(dev)
+    bps = args.blocks_per_split
+    ws = torch.empty(pda.pda_workspace_bytes(dims, bps) // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(w.num_seqs, w.num_q_heads, w.head_dim, dtype=torch.int16, device=dev)
+    kp, vp = pool.data_ptr() + 2 * w.k_base, pool.data_ptr() + 2 * w.v_base
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pda.pda_decode(dims, q, kp, vp, tables, counts, lastv, w.block_size, w.num_seqs,
+                       w.strides, ws, out, bps, stream)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    ms = wall * 1e3 / args.steps
+    nbytes = w.algorithmic_bytes()
+    tbs = nbytes / (ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    res = {
+        "metric": "paged decode attention achieved HBM TB/s (K+V+q+out bytes per call / time)",
+        "value": round(tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_call": round(ms * 1e3, 2),
+        "pct_of_peak": round(100 * tbs * 1e3 / PEAK_HBM_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "total_tokens": w.total_tokens,
+                   "algorithmic_bytes": nbytes, "layout": w.layout,
+                   "blocks_per_split": pda.pda_blocks_per_split(dims, bps),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "pda_decode step (partial + combine launches)",
+                     "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

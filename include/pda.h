@@ -1,0 +1,186 @@
+/*
+ * pda.h -- paged grouped-query decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpda.so.  One query token per sequence attends over a bf16 K/V
+ * cache stored in fixed-size pages ("blocks") that each sequence reaches
+ * through its own list of page ids.  The work runs as split-KV partial passes
+ * that keep an online-softmax (m, l, o) state, merged by log-sum-exp, then a
+ * finalize step that stores o / l as bf16.
+ *
+ * Sources, by page and section:
+ *  [TA]  spark_storage "tiled_attention.rs": the header comment (state
+ *        lifecycle: reset, one launch per tile, finalize), TiledAttentionDims
+ *        and its validate / gqa_ratio / *_bytes, TiledAttention::begin_step,
+ *        paged_strides, scratch_pool_strides, step_tile, finalize, and the
+ *        constant NEG_INF_F32_BITS.
+ *  [CK]  AstrAI "CUDA Kernels": section "Python Wrappers" (q/k/v layout
+ *        [batch, seq_len, n_heads, head_dim]; scale 1/sqrt(head_dim); wrappers
+ *        fail loudly when the compiled library is absent) and the "Overview"
+ *        table (GQA decode with split-KV; paged KV-cache decode).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device memory owned by the caller; the
+ *    library never allocates, frees or retains device memory and keeps no
+ *    global device state.  pda_plan is a small host-side handle.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued on it and the call returns without synchronising; a device
+ *    fault therefore surfaces at the caller's next synchronisation.
+ *  - Every argument is checked on the host before anything is enqueued: a
+ *    call that returns a status other than PDA_OK has enqueued nothing
+ *    (PDA_ERR_HIP excepted, which reports a failed launch).  A thread-local
+ *    text with details is available from pda_last_error().
+ *  - bf16 tensors hold raw bfloat16 bit patterns (uint16).  q, the pools, the
+ *    output, the state and the workspace must be 16-byte aligned; strides must
+ *    be multiples of 8 elements; page-id, count and last-valid arrays must be
+ *    4-byte aligned.
+ *  - Device-side data contract (not checkable on the host): counts are read
+ *    clamped to [0, tile_capacity] and last-valid counts to [0, block_size];
+ *    every listed page id must address a page inside the pools.
+ */
+#ifndef PDA_H
+#define PDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pda_status {
+    PDA_OK = 0,
+    PDA_ERR_NULL = 1,      /* a required pointer is NULL */
+    PDA_ERR_DIMS = 2,      /* a dimension is out of range (non-positive, or an index would overflow) */
+    PDA_ERR_GQA = 3,       /* num_q_heads is not a whole multiple of num_kv_heads ([TA] validate) */
+    PDA_ERR_HEAD_DIM = 4,  /* head_dim above 256 ([TA] validate) or not a multiple of 8 */
+    PDA_ERR_MAX_SEQS = 5,  /* num_seqs above max_seqs ([TA] begin_step) or negative */
+    PDA_ERR_ALIGN = 6,     /* pointer or stride misaligned, or stride negative */
+    PDA_ERR_WORKSPACE = 7, /* workspace smaller than pda_workspace_bytes requires */
+    PDA_ERR_HIP = 8        /* a HIP launch failed ([TA] begin_step memset status checks) */
+} pda_status;
+
+/* Sizes fixed for the lifetime of a plan ([TA] TiledAttentionDims).
+ * max_seqs bounds num_seqs of every call; tile_capacity is the row length of
+ * the page-id arrays, i.e. the most pages one sequence lists per call. */
+typedef struct pda_dims {
+    int32_t max_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t block_size;
+    int32_t tile_capacity;
+} pda_dims;
+
+/* Stride triple in bf16 elements selecting the K/V layout ([TA] paged_strides,
+ * scratch_pool_strides): element d of token slot j of kv head g in page b is
+ * at pool[b*blk + j*tok + g*kvh + d].  K and V share the triple. */
+typedef struct pda_strides {
+    int64_t blk;
+    int64_t tok;
+    int64_t kvh;
+} pda_strides;
+
+typedef struct pda_plan pda_plan;
+
+/* Checks dims: every field >= 1; num_q_heads % num_kv_heads == 0
+ * (PDA_ERR_GQA); head_dim <= 256 and head_dim % 8 == 0 (PDA_ERR_HEAD_DIM);
+ * tile_capacity * block_size <= 2^24 and tile_capacity * block_size^2 <= 2^32
+ * (PDA_ERR_DIMS).  [TA] TiledAttentionDims::validate. */
+pda_status pda_dims_validate(const pda_dims *dims);
+
+/* Bytes of the fp32 running state ([TA] m_bytes + l_bytes + o_bytes): m and l
+ * are [max_seqs, num_q_heads], o is [max_seqs, num_q_heads, head_dim], stored
+ * back to back in that order in one caller-owned device buffer.  m is in
+ * natural-log units (the running max of the scaled scores), l the running sum
+ * of exp(score - m), o the running sum of exp(score - m) * V.  0 if dims are
+ * invalid. */
+size_t pda_state_bytes(const pda_dims *dims);
+
+/* Byte offsets of m, l and o inside the state buffer (offsets[0..2]). */
+pda_status pda_state_offsets(const pda_dims *dims, size_t offsets[3]);
+
+/* Pages per split-KV partition that a call with `blocks_per_split` uses:
+ * the request clamped to [1, tile_capacity], or the library's own choice
+ * when the request is 0 (never fewer than ceil(tile_capacity / 64) pages). */
+int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
+
+/* Device workspace bytes for the split partials of max_seqs sequences with
+ * the given blocks_per_split (0 = the library's choice, sized for any device):
+ * max_seqs * num_q_heads * ceil(tile_capacity / bps) * (head_dim + 2) * 4.
+ * 0 if dims are invalid. */
+size_t pda_workspace_bytes(const pda_dims *dims, int32_t blocks_per_split);
+
+/* ([TA] paged_strides) layout [num_blocks, block_size, num_kv_heads, head_dim]:
+ * (block_size*num_kv_heads*head_dim, num_kv_heads*head_dim, head_dim). */
+pda_strides pda_paged_strides(const pda_dims *dims);
+
+/* ([TA] scratch_pool_strides) layout [slot, K|V, kv_head, block_size, head_dim]:
+ * with kv_stripe = num_kv_heads*block_size*head_dim,
+ * (2*kv_stripe, head_dim, block_size*head_dim).  The V pool pointer is the K
+ * pool pointer plus pda_scratch_pool_v_offset() elements. */
+pda_strides pda_scratch_pool_strides(const pda_dims *dims);
+int64_t pda_scratch_pool_v_offset(const pda_dims *dims);
+
+/* Creates a plan over caller-owned device buffers ([TA] TiledAttention::new,
+ * which allocates its own state; here the caller does):
+ *   state      device, pda_state_bytes(dims) bytes
+ *   workspace  device, at least pda_workspace_bytes(dims, blocks_per_split)
+ *   blocks_per_split  0 = the library's choice
+ * The buffers must outlive the plan.  *out receives the handle. */
+pda_status pda_create(const pda_dims *dims, void *state, void *workspace, size_t workspace_bytes,
+                      int32_t blocks_per_split, pda_plan **out);
+void pda_destroy(pda_plan *plan);
+
+/* Resets state rows [0, num_seqs) to m = -inf (bits 0xFF800000), l = 0,
+ * o = 0 ([TA] begin_step, NEG_INF_F32_BITS).  Rows >= num_seqs are left
+ * untouched.  Fails with PDA_ERR_MAX_SEQS if num_seqs > max_seqs. */
+pda_status pda_begin_step(pda_plan *plan, int32_t num_seqs, void *stream);
+
+/* Folds one tile of pages into the running state ([TA] step_tile; split-KV
+ * per [CK] Overview).
+ *   q                  device bf16 [num_seqs, num_q_heads, head_dim]
+ *   k_pool, v_pool     device bf16 pools addressed with `strides`
+ *   tile_blocks        device int32 [num_seqs, tile_capacity]: page ids, in
+ *                      logical token order
+ *   tile_block_counts  device int32 [num_seqs]: pages listed per sequence
+ *   last_block_valid   device int32 [num_seqs], or NULL to use
+ *                      last_block_valid_default for every sequence: valid
+ *                      token slots in the last page this tile lists for the
+ *                      sequence (block_size when the sequence continues in a
+ *                      later tile)
+ * q head h attends with kv head h / (num_q_heads / num_kv_heads); scores are
+ * scaled by 1/sqrt(head_dim) ([CK] Python Wrappers).  A sequence with count
+ * 0 leaves its state rows bit-unchanged.  Rows >= num_seqs are untouched. */
+pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *tile_blocks, const int32_t *tile_block_counts,
+                         const int32_t *last_block_valid, int32_t last_block_valid_default,
+                         int32_t num_seqs, pda_strides strides, void *stream);
+
+/* out[s, h, :] = bf16(o / l), rounded to nearest even; 0 where l == 0
+ * ([TA] finalize).  out: device bf16 [num_seqs, num_q_heads, head_dim]. */
+pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *stream);
+
+/* One-shot decode: reset, one tile, finalize in two launches, with the
+ * split partials in `workspace` ([CK] Overview: paged decode, split-KV).
+ * Arguments as pda_step_tile plus:
+ *   dims        as for pda_create (num_seqs <= dims->max_seqs)
+ *   workspace   device, at least pda_workspace_bytes(dims, blocks_per_split)
+ *   out         device bf16 [num_seqs, num_q_heads, head_dim]
+ * A sequence with no token gets an all-zero output row. */
+pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
+                      const int32_t *block_tables, const int32_t *block_counts,
+                      const int32_t *last_block_valid, int32_t last_block_valid_default,
+                      int32_t num_seqs, pda_strides strides, void *workspace,
+                      size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream);
+
+/* Static name of a status code. */
+const char *pda_status_string(pda_status status);
+
+/* Details of the last failure on the calling thread ("" if none). */
+const char *pda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDA_H */

@@ -1,0 +1,232 @@
+"""Python binding of libpda.so: paged grouped-query decode attention on MI355X.
+
+Argument marshalling only.  Every function has the name and the argument
+order of the C entry point it calls (``include/pda.h``); every step of the
+computation runs in the library's gfx950 kernels.  Device buffers are passed
+as torch tensors (or raw integer addresses); torch provides device memory and
+streams and nothing else.  A status other than PDA_OK raises ``PdaError`` (a
+RuntimeError carrying the status code and the library's detail text).  If the
+compiled library is missing the import fails with RuntimeError; there is no
+fallback of any kind, as for the AstrAI page's wrappers ("CUDA Kernels",
+section "Python Wrappers", which raise when their .so is absent).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own copy of the HIP runtime (loaded by file name, under the
+# same SONAME as the system's).  Loading torch first makes libpda.so bind to
+# that very runtime instance, so the device memory and streams torch hands out
+# are valid inside the library; loaded the other way round the process would
+# hold two HIP runtimes and the library would see no device.
+import torch  # noqa: F401
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpda.so")
+
+if not os.path.exists(LIB_PATH):
+    raise RuntimeError(
+        f"{LIB_PATH} is missing: build it with `python paged_gqa_decode_pda_amd/build.py` "
+        "(or __graft_entry__.build()); there is no fallback path")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PDA_OK = 0
+STATUS_NAMES = ["PDA_OK", "PDA_ERR_NULL", "PDA_ERR_DIMS", "PDA_ERR_GQA", "PDA_ERR_HEAD_DIM",
+                "PDA_ERR_MAX_SEQS", "PDA_ERR_ALIGN", "PDA_ERR_WORKSPACE", "PDA_ERR_HIP"]
+for _i, _n in enumerate(STATUS_NAMES):
+    globals()[_n] = _i
+
+EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_blocks_per_split",
+            "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
+            "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
+            "pda_step_tile", "pda_finalize", "pda_decode", "pda_status_string", "pda_last_error"]
+
+
+class pda_dims(ctypes.Structure):
+    _fields_ = [("max_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("tile_capacity", ctypes.c_int32)]
+
+
+class pda_strides(ctypes.Structure):
+    _fields_ = [("blk", ctypes.c_int64), ("tok", ctypes.c_int64), ("kvh", ctypes.c_int64)]
+
+    def astuple(self):
+        return (self.blk, self.tok, self.kvh)
+
+
+class PdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {detail}")
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_PD = ctypes.POINTER(pda_dims)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_sig("pda_dims_validate", ctypes.c_int, _PD)
+_sig("pda_state_bytes", _sz, _PD)
+_sig("pda_state_offsets", ctypes.c_int, _PD, ctypes.POINTER(_sz))
+_sig("pda_blocks_per_split", _i32, _PD, _i32)
+_sig("pda_workspace_bytes", _sz, _PD, _i32)
+_sig("pda_paged_strides", pda_strides, _PD)
+_sig("pda_scratch_pool_strides", pda_strides, _PD)
+_sig("pda_scratch_pool_v_offset", _i64, _PD)
+_sig("pda_create", ctypes.c_int, _PD, _P, _P, _sz, _i32, ctypes.POINTER(_P))
+_sig("pda_destroy", None, _P)
+_sig("pda_begin_step", ctypes.c_int, _P, _i32, _P)
+_sig("pda_step_tile", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P)
+_sig("pda_finalize", ctypes.c_int, _P, _P, _i32, _P)
+_sig("pda_decode", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P, _sz,
+     _P, _i32, _P)
+_sig("pda_status_string", ctypes.c_char_p, ctypes.c_int)
+_sig("pda_last_error", ctypes.c_char_p)
+
+
+def _dims(d) -> pda_dims:
+    if isinstance(d, pda_dims):
+        return d
+    if isinstance(d, dict):
+        return pda_dims(**d)
+    return pda_dims(*d)
+
+
+def _strides(s) -> pda_strides:
+    if isinstance(s, pda_strides):
+        return s
+    return pda_strides(*[int(x) for x in s])
+
+
+def _addr(x):
+    """Device address of a tensor (its data_ptr) or an integer address; None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _nbytes(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        raise TypeError("pass the byte count explicitly with an integer address")
+    return x.numel() * x.element_size()
+
+
+def _stream(s):
+    """hipStream_t handle: None -> torch's current stream on the current device."""
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int):
+    if status != PDA_OK:
+        raise PdaError(status, _lib.pda_last_error().decode())
+
+
+def pda_status_string(status: int) -> str:
+    return _lib.pda_status_string(status).decode()
+
+
+def pda_last_error() -> str:
+    return _lib.pda_last_error().decode()
+
+
+def pda_dims_validate(dims) -> None:
+    d = _dims(dims)
+    _check(_lib.pda_dims_validate(ctypes.byref(d)))
+
+
+def pda_state_bytes(dims) -> int:
+    d = _dims(dims)
+    return _lib.pda_state_bytes(ctypes.byref(d))
+
+
+def pda_state_offsets(dims):
+    d = _dims(dims)
+    off = (_sz * 3)()
+    _check(_lib.pda_state_offsets(ctypes.byref(d), off))
+    return tuple(off)
+
+
+def pda_blocks_per_split(dims, blocks_per_split: int = 0) -> int:
+    d = _dims(dims)
+    return _lib.pda_blocks_per_split(ctypes.byref(d), blocks_per_split)
+
+
+def pda_workspace_bytes(dims, blocks_per_split: int = 0) -> int:
+    d = _dims(dims)
+    return _lib.pda_workspace_bytes(ctypes.byref(d), blocks_per_split)
+
+
+def pda_paged_strides(dims):
+    d = _dims(dims)
+    return _lib.pda_paged_strides(ctypes.byref(d)).astuple()
+
+
+def pda_scratch_pool_strides(dims):
+    d = _dims(dims)
+    return _lib.pda_scratch_pool_strides(ctypes.byref(d)).astuple()
+
+
+def pda_scratch_pool_v_offset(dims) -> int:
+    d = _dims(dims)
+    return _lib.pda_scratch_pool_v_offset(ctypes.byref(d))
+
+
+def pda_create(dims, state, workspace, blocks_per_split: int = 0, workspace_bytes=None) -> int:
+    """Returns the plan handle (an integer host address)."""
+    d = _dims(dims)
+    out = _P()
+    nb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    _check(_lib.pda_create(ctypes.byref(d), _addr(state), _addr(workspace), nb, blocks_per_split,
+                           ctypes.byref(out)))
+    return out.value
+
+
+def pda_destroy(plan) -> None:
+    _lib.pda_destroy(plan)
+
+
+def pda_begin_step(plan, num_seqs: int, stream=None) -> None:
+    _check(_lib.pda_begin_step(plan, num_seqs, _stream(stream)))
+
+
+def pda_step_tile(plan, q, k_pool, v_pool, tile_blocks, tile_block_counts, last_block_valid,
+                  last_block_valid_default: int, num_seqs: int, strides, stream=None) -> None:
+    _check(_lib.pda_step_tile(plan, _addr(q), _addr(k_pool), _addr(v_pool), _addr(tile_blocks),
+                              _addr(tile_block_counts), _addr(last_block_valid),
+                              last_block_valid_default, num_seqs, _strides(strides),
+                              _stream(stream)))
+
+
+def pda_finalize(plan, out, num_seqs: int, stream=None) -> None:
+    _check(_lib.pda_finalize(plan, _addr(out), num_seqs, _stream(stream)))
+
+
+def pda_decode(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+               last_block_valid_default: int, num_seqs: int, strides, workspace, out,
+               blocks_per_split: int = 0, stream=None, workspace_bytes=None) -> None:
+    d = _dims(dims)
+    nb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    _check(_lib.pda_decode(ctypes.byref(d), _addr(q), _addr(k_pool), _addr(v_pool),
+                           _addr(block_tables), _addr(block_counts), _addr(last_block_valid),
+                           last_block_valid_default, num_seqs, _strides(strides), _addr(workspace),
+                           nb, _addr(out), blocks_per_split, _stream(stream)))

@@ -1,0 +1,43 @@
+"""Build libpda.so (the gfx950 HIP kernels and the C ABI of include/pda.h) in-tree.
+
+    python paged_gqa_decode_pda_amd/build.py
+
+Run as a script (the package itself refuses to import until the library
+exists).
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+LIB_PATH = os.path.join(HERE, "libpda.so")
+SOURCES = [os.path.join(HERE, "csrc", "pda_api.hip"), os.path.join(HERE, "csrc", "pda_kernels.hip")]
+ARCH = "gfx950"
+
+# Packed-fp32 VALU forms are disabled for every HIP translation unit; hipcc's
+# host pass warns that it does not know the feature, which is harmless.
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if cand and (os.path.sep not in cand or os.path.exists(cand)):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build(verbose=True, extra=sys.argv[1:])

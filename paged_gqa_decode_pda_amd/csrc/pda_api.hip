@@ -1,0 +1,390 @@
+// Host side of the C ABI declared in include/pda.h: argument validation, split
+// planning and kernel launches.  Nothing here allocates device memory or
+// synchronises; every check runs before the first enqueue.
+#include "../../include/pda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "pda_internal.h"
+
+struct pda_plan {
+    pda_dims dims;
+    float *m, *l, *o;
+    void *workspace;
+    size_t workspace_bytes;
+    int32_t bps_request;
+};
+
+namespace {
+
+thread_local char g_err[512];
+
+pda_status fail(pda_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+pda_status check_dims(const pda_dims *d) {
+    if (!d) return fail(PDA_ERR_NULL, "dims is NULL");
+    if (d->max_seqs < 1 || d->num_q_heads < 1 || d->num_kv_heads < 1 || d->head_dim < 1 ||
+        d->block_size < 1 || d->tile_capacity < 1)
+        return fail(PDA_ERR_DIMS, "every dimension must be >= 1");
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(PDA_ERR_GQA, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->head_dim > 256) return fail(PDA_ERR_HEAD_DIM, "head_dim %d exceeds 256", d->head_dim);
+    if (d->head_dim % 8 != 0)
+        return fail(PDA_ERR_HEAD_DIM, "head_dim %d is not a multiple of 8", d->head_dim);
+    const int64_t tile_tokens = (int64_t)d->tile_capacity * d->block_size;
+    if (tile_tokens > (int64_t(1) << 24) ||
+        (uint64_t)tile_tokens * (uint64_t)d->block_size > (uint64_t(1) << 32))
+        return fail(PDA_ERR_DIMS, "tile_capacity * block_size too large");
+    const int64_t G = d->num_q_heads / d->num_kv_heads;
+    const pda::Plan p = pda::choose_plan((int)G, d->head_dim, d->block_size);
+    if ((int64_t)d->num_kv_heads * p.nhc > 65535 || d->max_seqs > 65535)
+        return fail(PDA_ERR_DIMS, "num_kv_heads * head chunks and max_seqs must be <= 65535");
+    return PDA_OK;
+}
+
+int32_t min_auto_bps(const pda_dims *d) {
+    const int32_t lo = (int32_t)ceil_div(d->tile_capacity, 64);
+    return lo < 1 ? 1 : lo;
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return 256;
+    return cus;
+}
+
+// Pages per split.  An explicit request is clamped to [1, tile_capacity].
+// Otherwise: the smallest power-of-two multiple of 8 pages (never below
+// ceil(cap / 64)) for which the workgroups of full-length sequences would
+// number at least 4 per compute unit, capped at the tile capacity.
+int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
+    const int32_t cap = d->tile_capacity;
+    if (request > 0) return request > cap ? cap : request;
+    const int32_t lo = min_auto_bps(d);
+    const int64_t G = d->num_q_heads / d->num_kv_heads;
+    const pda::Plan p = pda::choose_plan((int)G, d->head_dim, d->block_size);
+    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * d->num_kv_heads * p.nhc;
+    const int64_t target = 4 * (int64_t)device_cus();
+    int32_t bps = 8;
+    while (bps < cap && units * ceil_div(cap, bps) > target && bps < 64) bps *= 2;
+    if (bps < lo) bps = lo;
+    if (bps > cap) bps = cap;
+    return bps;
+}
+
+size_t workspace_for(const pda_dims *d, int32_t bps, int64_t seqs) {
+    const int64_t nsplit = ceil_div(d->tile_capacity, bps);
+    return (size_t)seqs * d->num_q_heads * nsplit * (d->head_dim + 2) * sizeof(float);
+}
+
+pda_status check_strides(const pda_dims *d, pda_strides st) {
+    if (st.blk < 0 || st.tok < 0 || st.kvh < 0)
+        return fail(PDA_ERR_ALIGN, "strides must be non-negative");
+    if (st.blk % 8 || st.tok % 8 || st.kvh % 8)
+        return fail(PDA_ERR_ALIGN, "strides (%lld, %lld, %lld) must be multiples of 8 elements",
+                    (long long)st.blk, (long long)st.tok, (long long)st.kvh);
+    const int64_t in_page = (int64_t)(d->block_size - 1) * st.tok +
+                            (int64_t)(d->num_kv_heads - 1) * st.kvh + d->head_dim;
+    if (in_page >= (int64_t(1) << 31))
+        return fail(PDA_ERR_DIMS, "a token row offset inside a page exceeds 2^31 elements");
+    return PDA_OK;
+}
+
+pda_status check_tile_ptrs(const void *q, const void *k, const void *v, const int32_t *blocks,
+                           const int32_t *counts, const int32_t *lastv) {
+    if (!q || !k || !v || !blocks || !counts) return fail(PDA_ERR_NULL, "a required pointer is NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16))
+        return fail(PDA_ERR_ALIGN, "q, k_pool and v_pool must be 16-byte aligned");
+    if (!aligned(blocks, 4) || !aligned(counts, 4) || (lastv && !aligned(lastv, 4)))
+        return fail(PDA_ERR_ALIGN, "page-id, count and last-valid arrays must be 4-byte aligned");
+    return PDA_OK;
+}
+
+pda::PartialArgs partial_args(const pda_dims *d, const void *q, const void *k, const void *v,
+                              const int32_t *blocks, const int32_t *counts, const int32_t *lastv,
+                              int32_t lv_default, pda_strides st, int32_t bps, void *ws, int S,
+                              const pda::Plan &p) {
+    pda::PartialArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.blocks = blocks;
+    a.counts = counts;
+    a.lastv = lastv;
+    a.blk = st.blk;
+    a.tok = st.tok;
+    a.kvh = st.kvh;
+    a.bs_magic = ((uint64_t(1) << 32) + (uint64_t)d->block_size - 1) / (uint64_t)d->block_size;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = d->num_q_heads / d->num_kv_heads;
+    a.D = d->head_dim;
+    a.bs = d->block_size;
+    a.cap = d->tile_capacity;
+    a.bps = bps;
+    a.nhc = p.nhc;
+    a.nsplit = (int32_t)ceil_div(d->tile_capacity, bps);
+    a.lv_default = lv_default;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
+    float *wsf = static_cast<float *>(ws);
+    a.part_o = wsf;
+    a.part_ml = wsf + (int64_t)S * d->num_q_heads * a.nsplit * d->head_dim;
+    return a;
+}
+
+pda::CombineArgs combine_args(const pda::PartialArgs &pa, int S) {
+    pda::CombineArgs c;
+    c.counts = pa.counts;
+    c.lastv = pa.lastv;
+    c.part_ml = pa.part_ml;
+    c.part_o = pa.part_o;
+    c.m = c.l = c.o = nullptr;
+    c.out = nullptr;
+    c.S = S;
+    c.Hq = pa.Hq;
+    c.D = pa.D;
+    c.bs = pa.bs;
+    c.cap = pa.cap;
+    c.bps = pa.bps;
+    c.nsplit = pa.nsplit;
+    c.lv_default = pa.lv_default;
+    return c;
+}
+
+pda_status hip_fail(hipError_t e, const char *what) {
+    return fail(PDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+pda_status pda_dims_validate(const pda_dims *dims) {
+    clear_err();
+    return check_dims(dims);
+}
+
+size_t pda_state_bytes(const pda_dims *d) {
+    if (check_dims(d) != PDA_OK) return 0;
+    const size_t rows = (size_t)d->max_seqs * d->num_q_heads;
+    return rows * sizeof(float) * (2 + (size_t)d->head_dim);
+}
+
+pda_status pda_state_offsets(const pda_dims *d, size_t offsets[3]) {
+    clear_err();
+    pda_status st = check_dims(d);
+    if (st != PDA_OK) return st;
+    if (!offsets) return fail(PDA_ERR_NULL, "offsets is NULL");
+    const size_t rows = (size_t)d->max_seqs * d->num_q_heads;
+    offsets[0] = 0;
+    offsets[1] = rows * sizeof(float);
+    offsets[2] = 2 * rows * sizeof(float);
+    return PDA_OK;
+}
+
+int32_t pda_blocks_per_split(const pda_dims *d, int32_t request) {
+    if (check_dims(d) != PDA_OK) return 0;
+    return resolve_bps(d, request, d->max_seqs);
+}
+
+size_t pda_workspace_bytes(const pda_dims *d, int32_t request) {
+    if (check_dims(d) != PDA_OK) return 0;
+    const int32_t bps = request > 0 ? (request > d->tile_capacity ? d->tile_capacity : request)
+                                    : min_auto_bps(d);
+    return workspace_for(d, bps, d->max_seqs);
+}
+
+pda_strides pda_paged_strides(const pda_dims *d) {
+    pda_strides s{0, 0, 0};
+    if (!d) return s;
+    s.blk = (int64_t)d->block_size * d->num_kv_heads * d->head_dim;
+    s.tok = (int64_t)d->num_kv_heads * d->head_dim;
+    s.kvh = d->head_dim;
+    return s;
+}
+
+pda_strides pda_scratch_pool_strides(const pda_dims *d) {
+    pda_strides s{0, 0, 0};
+    if (!d) return s;
+    const int64_t stripe = (int64_t)d->num_kv_heads * d->block_size * d->head_dim;
+    s.blk = 2 * stripe;
+    s.tok = d->head_dim;
+    s.kvh = (int64_t)d->block_size * d->head_dim;
+    return s;
+}
+
+int64_t pda_scratch_pool_v_offset(const pda_dims *d) {
+    if (!d) return 0;
+    return (int64_t)d->num_kv_heads * d->block_size * d->head_dim;
+}
+
+pda_status pda_create(const pda_dims *dims, void *state, void *workspace, size_t workspace_bytes,
+                      int32_t blocks_per_split, pda_plan **out) {
+    clear_err();
+    pda_status st = check_dims(dims);
+    if (st != PDA_OK) return st;
+    if (!state || !out) return fail(PDA_ERR_NULL, "state and out must be non-NULL");
+    if (!aligned(state, 16)) return fail(PDA_ERR_ALIGN, "state must be 16-byte aligned");
+    if (blocks_per_split < 0) return fail(PDA_ERR_DIMS, "blocks_per_split must be >= 0");
+    if (workspace && !aligned(workspace, 16))
+        return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t need = pda_workspace_bytes(dims, blocks_per_split);
+    if (!workspace || workspace_bytes < need)
+        return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    pda_plan *p = new (std::nothrow) pda_plan;
+    if (!p) return fail(PDA_ERR_DIMS, "out of host memory");
+    p->dims = *dims;
+    const size_t rows = (size_t)dims->max_seqs * dims->num_q_heads;
+    p->m = static_cast<float *>(state);
+    p->l = p->m + rows;
+    p->o = p->l + rows;
+    p->workspace = workspace;
+    p->workspace_bytes = workspace_bytes;
+    p->bps_request = blocks_per_split;
+    *out = p;
+    return PDA_OK;
+}
+
+void pda_destroy(pda_plan *plan) { delete plan; }
+
+pda_status pda_begin_step(pda_plan *plan, int32_t num_seqs, void *stream) {
+    clear_err();
+    if (!plan) return fail(PDA_ERR_NULL, "plan is NULL");
+    if (num_seqs < 0 || num_seqs > plan->dims.max_seqs)
+        return fail(PDA_ERR_MAX_SEQS, "begin_step num_seqs %d outside [0, max_seqs=%d]", num_seqs,
+                    plan->dims.max_seqs);
+    if (num_seqs == 0) return PDA_OK;
+    hipError_t e = pda::launch_reset(plan->m, plan->l, plan->o,
+                                     (int64_t)num_seqs * plan->dims.num_q_heads, plan->dims.head_dim,
+                                     static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "reset launch");
+}
+
+pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *tile_blocks, const int32_t *tile_block_counts,
+                         const int32_t *last_block_valid, int32_t last_block_valid_default,
+                         int32_t num_seqs, pda_strides strides, void *stream) {
+    clear_err();
+    if (!plan) return fail(PDA_ERR_NULL, "plan is NULL");
+    const pda_dims *d = &plan->dims;
+    if (num_seqs < 0 || num_seqs > d->max_seqs)
+        return fail(PDA_ERR_MAX_SEQS, "num_seqs %d outside [0, max_seqs=%d]", num_seqs, d->max_seqs);
+    pda_status st = check_tile_ptrs(q, k_pool, v_pool, tile_blocks, tile_block_counts, last_block_valid);
+    if (st != PDA_OK) return st;
+    if ((st = check_strides(d, strides)) != PDA_OK) return st;
+    if (num_seqs == 0) return PDA_OK;
+    const int32_t bps = resolve_bps(d, plan->bps_request, num_seqs);
+    if (ceil_div(d->tile_capacity, bps) > 65535)
+        return fail(PDA_ERR_DIMS, "more than 65535 splits per sequence; raise blocks_per_split");
+    if (workspace_for(d, bps, num_seqs) > plan->workspace_bytes)
+        return fail(PDA_ERR_WORKSPACE, "workspace too small for %d sequences", num_seqs);
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const pda::Plan p = pda::choose_plan(G, d->head_dim, d->block_size);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    pda::PartialArgs a = partial_args(d, q, k_pool, v_pool, tile_blocks, tile_block_counts,
+                                      last_block_valid, last_block_valid_default, strides, bps,
+                                      plan->workspace, num_seqs, p);
+    hipError_t e = pda::launch_partial(p, a, num_seqs, hs);
+    if (e != hipSuccess) return hip_fail(e, "partial launch");
+    pda::CombineArgs c = combine_args(a, num_seqs);
+    c.m = plan->m;
+    c.l = plan->l;
+    c.o = plan->o;
+    e = pda::launch_combine(c, p.dp, hs);
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "merge launch");
+}
+
+pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *stream) {
+    clear_err();
+    if (!plan) return fail(PDA_ERR_NULL, "plan is NULL");
+    if (num_seqs < 0 || num_seqs > plan->dims.max_seqs)
+        return fail(PDA_ERR_MAX_SEQS, "num_seqs %d outside [0, max_seqs=%d]", num_seqs,
+                    plan->dims.max_seqs);
+    if (!out) return fail(PDA_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if (num_seqs == 0) return PDA_OK;
+    hipError_t e = pda::launch_finalize(plan->l, plan->o, static_cast<uint16_t *>(out),
+                                        (int64_t)num_seqs * plan->dims.num_q_heads,
+                                        plan->dims.head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "finalize launch");
+}
+
+pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
+                      const int32_t *block_tables, const int32_t *block_counts,
+                      const int32_t *last_block_valid, int32_t last_block_valid_default,
+                      int32_t num_seqs, pda_strides strides, void *workspace,
+                      size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream) {
+    clear_err();
+    pda_status st = check_dims(dims);
+    if (st != PDA_OK) return st;
+    if (num_seqs < 0 || num_seqs > dims->max_seqs)
+        return fail(PDA_ERR_MAX_SEQS, "num_seqs %d outside [0, max_seqs=%d]", num_seqs, dims->max_seqs);
+    if (blocks_per_split < 0) return fail(PDA_ERR_DIMS, "blocks_per_split must be >= 0");
+    if ((st = check_tile_ptrs(q, k_pool, v_pool, block_tables, block_counts, last_block_valid)) != PDA_OK)
+        return st;
+    if (!out) return fail(PDA_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if ((st = check_strides(dims, strides)) != PDA_OK) return st;
+    if (workspace && !aligned(workspace, 16))
+        return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (num_seqs == 0) return PDA_OK;
+    const int32_t bps = resolve_bps(dims, blocks_per_split, num_seqs);
+    if (ceil_div(dims->tile_capacity, bps) > 65535)
+        return fail(PDA_ERR_DIMS, "more than 65535 splits per sequence; raise blocks_per_split");
+    const size_t need = workspace_for(dims, bps, num_seqs);
+    if (!workspace || workspace_bytes < need)
+        return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    const int G = dims->num_q_heads / dims->num_kv_heads;
+    const pda::Plan p = pda::choose_plan(G, dims->head_dim, dims->block_size);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    pda::PartialArgs a = partial_args(dims, q, k_pool, v_pool, block_tables, block_counts,
+                                      last_block_valid, last_block_valid_default, strides, bps,
+                                      workspace, num_seqs, p);
+    hipError_t e = pda::launch_partial(p, a, num_seqs, hs);
+    if (e != hipSuccess) return hip_fail(e, "partial launch");
+    pda::CombineArgs c = combine_args(a, num_seqs);
+    c.out = static_cast<uint16_t *>(out);
+    e = pda::launch_combine(c, p.dp, hs);
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "combine launch");
+}
+
+const char *pda_status_string(pda_status s) {
+    switch (s) {
+        case PDA_OK: return "PDA_OK";
+        case PDA_ERR_NULL: return "PDA_ERR_NULL";
+        case PDA_ERR_DIMS: return "PDA_ERR_DIMS";
+        case PDA_ERR_GQA: return "PDA_ERR_GQA";
+        case PDA_ERR_HEAD_DIM: return "PDA_ERR_HEAD_DIM";
+        case PDA_ERR_MAX_SEQS: return "PDA_ERR_MAX_SEQS";
+        case PDA_ERR_ALIGN: return "PDA_ERR_ALIGN";
+        case PDA_ERR_WORKSPACE: return "PDA_ERR_WORKSPACE";
+        case PDA_ERR_HIP: return "PDA_ERR_HIP";
+    }
+    return "PDA_ERR_UNKNOWN";
+}
+
+const char *pda_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,279 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every test prints the case it is about to launch before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_harness import Device, assert_parity, out_bits, out_to_f64
+from helpers import build_case
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(*what):
+    print("CASE", *what, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_of(dev: Device, tiles=None):
+    p = dev.p
+    b, c, v = p.blocks, p.counts, p.lastv
+    if tiles is not None:
+        b, c, v = b[:tiles], c[:tiles], v[:tiles]
+    return oracle.attend(p.q, p.pool, p.k_base, p.v_base, p.strides, p.Hkv, p.bs, b, c, v)
+
+
+def test_config1_decode_and_tiled():
+    announce("cfg1 decode + tiled")
+    w = workloads.config(1)
+    dev = Device(w)
+    ref = oracle.attend_workload(w)
+    got = out_to_f64(dev.decode())
+    e = assert_parity(got, ref["out"], label="cfg1 decode")
+    state, out = dev.tiled()
+    assert_parity(out_to_f64(out), ref["out"], label="cfg1 tiled")
+    m, l, o = dev.split_state(state)
+    # state: natural-log max, and l, o relative to it
+    np.testing.assert_allclose(m, ref["m"], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(l * np.exp(m - ref["m"]), ref["l"], rtol=1e-4)
+    np.testing.assert_allclose(o / l[..., None], ref["out"], rtol=0, atol=1e-4)
+    print("cfg1 max/mean err", e)
+
+
+SMALL = [
+    # S, Hq, Hkv, D, bs, contexts, layout, tiles
+    (1, 4, 1, 64, 16, [100], "paged", 1),
+    (3, 8, 2, 128, 16, [1, 37, 300], "paged", 1),
+    (3, 8, 8, 128, 16, [5, 0, 64], "scratch", 2),
+    (2, 16, 8, 256, 16, [129, 200], "paged", 3),
+    (4, 8, 1, 64, 8, [9, 17, 1, 90], "paged", 2),
+    (2, 4, 4, 128, 1, [7, 33], "scratch", 1),
+    (2, 12, 4, 96, 32, [70, 3], "paged", 2),
+    (2, 16, 2, 64, 16, [50, 81], "paged", 1),
+    (2, 32, 4, 128, 16, [130, 47], "scratch", 1),
+    (1, 6, 2, 200, 5, [61], "paged", 1),
+    (2, 4, 2, 8, 4, [13, 2], "paged", 1),
+    (3, 8, 4, 256, 32, [100, 1, 65], "scratch", 2),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s[:5])) + f"-{s[6]}-t{s[7]}")
+@pytest.mark.parametrize("bps", [0, 1, 3])
+def test_small_shapes(shape, bps):
+    S, Hq, Hkv, D, bs, ctx, layout, T = shape
+    announce("small", shape, "bps", bps)
+    rng = np.random.Generator(np.random.PCG64(hash((S, Hq, Hkv, D, bs, T)) % (1 << 32)))
+    case = build_case(rng, S, Hq, Hkv, D, bs, ctx, layout=layout, n_tiles=T)
+    dev = Device(case)
+    ref_all = oracle_of(dev)
+    state, out = dev.tiled(bps=bps)
+    assert_parity(out_to_f64(out), ref_all["out"], label=f"tiled {shape}")
+    if T == 1:
+        got = out_to_f64(dev.decode(bps=bps))
+        assert_parity(got, ref_all["out"], label=f"decode {shape}")
+
+
+def test_context_one_bit_exact():
+    announce("context 1 bit-exact")
+    rng = np.random.Generator(np.random.PCG64(31))
+    for layout in ("paged", "scratch"):
+        for D in (64, 128, 256):
+            case = build_case(rng, 3, 8, 2, D, 16, [1, 1, 1], layout=layout)
+            dev = Device(case)
+            want = np.stack([np.stack([workloads.f32_to_bf16_bits(case.V[s][0, h // 4])
+                                       for h in range(8)]) for s in range(3)])
+            np.testing.assert_array_equal(out_bits(dev.decode()), want)
+            _, out = dev.tiled()
+            np.testing.assert_array_equal(out_bits(out), want)
+
+
+def test_exact_token_count_and_sums():
+    """q = 0 gives every token weight exactly 1: l must equal the token count
+    and o the exact integer sum of V (no token dropped or repeated)."""
+    announce("exact counts")
+    rng = np.random.Generator(np.random.PCG64(32))
+    for (S, Hq, Hkv, D, bs, ctx, T) in [(3, 8, 2, 128, 16, [1000, 17, 513], 3),
+                                       (2, 4, 1, 64, 8, [99, 250], 2),
+                                       (2, 4, 2, 256, 16, [700, 33], 4)]:
+        case = build_case(rng, S, Hq, Hkv, D, bs, ctx, n_tiles=T, q_values=np.zeros((S, Hq, D)),
+                          values=lambda s, n: (rng.standard_normal((n, Hkv, D)),
+                                               rng.integers(-4, 5, size=(n, Hkv, D)).astype(float)))
+        dev = Device(case)
+        for bps in (0, 1, 5):
+            state, _ = dev.tiled(bps=bps)
+            m, l, o = dev.split_state(state)
+            G = Hq // Hkv
+            for s in range(S):
+                np.testing.assert_array_equal(m[s], 0.0)
+                np.testing.assert_array_equal(l[s], float(ctx[s]))
+                for h in range(Hq):
+                    np.testing.assert_array_equal(o[s, h], case.V[s][:, h // G].sum(axis=0))
+
+
+def test_page_permutation_bit_identical():
+    announce("page permutation")
+    rng = np.random.Generator(np.random.PCG64(33))
+    case = build_case(rng, 3, 8, 2, 128, 16, [200, 33, 90], extra_pages=5)
+    a = out_bits(Device(case).decode())
+    P, blk = case.num_pages, case.strides[0]
+    perm = rng.permutation(P)
+    pool = case.pool.copy()
+    for base in (case.k_base, case.v_base):
+        pool[base:base + P * blk].reshape(P, blk)[perm] = case.pool[base:base + P * blk].reshape(P, blk)
+    case.pool = pool
+    case.blocks = perm[case.blocks].astype(np.int32)
+    b = out_bits(Device(case).decode())
+    np.testing.assert_array_equal(a, b)
+
+
+def test_repeat_runs_bit_stable():
+    announce("repeat-run stability")
+    rng = np.random.Generator(np.random.PCG64(34))
+    case = build_case(rng, 4, 32, 8, 128, 16, [3000, 17, 900, 2048], n_tiles=2)
+    dev = Device(case)
+    outs, states = set(), set()
+    for _ in range(10):
+        state, out = dev.tiled()
+        states.add(state.cpu().numpy().tobytes())
+        outs.add(out_bits(out).tobytes())
+    assert len(outs) == 1 and len(states) == 1
+    d = {out_bits(dev.decode(tile=0)).tobytes() for _ in range(5)}
+    assert len(d) == 1
+
+
+def test_paged_and_scratch_bit_identical():
+    announce("paged vs scratch")
+    res = []
+    for layout in ("paged", "scratch"):
+        rng = np.random.Generator(np.random.PCG64(35))
+        case = build_case(rng, 3, 16, 4, 128, 16, [150, 64, 9], layout=layout, n_tiles=2)
+        dev = Device(case)
+        _, out = dev.tiled()
+        res.append(out_bits(out))
+    np.testing.assert_array_equal(res[0], res[1])
+
+
+def test_empty_tile_leaves_state_unchanged_and_canary_rows():
+    announce("empty tile + canaries")
+    rng = np.random.Generator(np.random.PCG64(36))
+    case = build_case(rng, 3, 8, 2, 64, 16, [40, 0, 70], tile_sizes=[[2, 0, 3], [0, 0, 0], [1, 0, 2]])
+    dev = Device(case, max_seqs=5)
+    state = dev.new_state()
+    state.fill_(7.0)
+    out = dev.new_out(0x1234)
+    pda = dev.pda
+    ws = dev.workspace()
+    plan = dev.plan(state, ws)
+    try:
+        pda.pda_begin_step(plan, 3)
+        pda.pda_step_tile(plan, dev.q, dev.kp, dev.vp, dev.blocks[0], dev.counts[0], dev.lastv[0], 16,
+                          3, case.strides)
+        dev.torch.cuda.synchronize()
+        before = state.cpu().numpy().copy()
+        pda.pda_step_tile(plan, dev.q, dev.kp, dev.vp, dev.blocks[1], dev.counts[1], dev.lastv[1], 16,
+                          3, case.strides)
+        dev.torch.cuda.synchronize()
+        np.testing.assert_array_equal(before, state.cpu().numpy())
+        pda.pda_step_tile(plan, dev.q, dev.kp, dev.vp, dev.blocks[2], dev.counts[2], dev.lastv[2], 16,
+                          3, case.strides)
+        pda.pda_finalize(plan, out, 3)
+        dev.torch.cuda.synchronize()
+    finally:
+        pda.pda_destroy(plan)
+    m, l, o = dev.split_state(state)
+    assert np.all(m[3:] == 7.0) and np.all(l[3:] == 7.0) and np.all(o[3:] == 7.0)
+    ob = out_bits(out)
+    assert np.all(ob[3:] == 0x1234)
+    assert np.all(ob[1] == 0) and np.all(np.isneginf(m[1])) and np.all(l[1] == 0)
+    ref = oracle_of(dev)
+    assert_parity(out_to_f64(out)[:3], ref["out"], label="empty-tile case")
+
+
+def test_checkpoint_resume_bit_identical():
+    announce("checkpoint/resume")
+    rng = np.random.Generator(np.random.PCG64(37))
+    case = build_case(rng, 2, 8, 2, 128, 16, [500, 260], n_tiles=4)
+    dev = Device(case)
+    s_full, o_full = dev.tiled()
+    state = dev.new_state()
+    ws = dev.workspace()
+    plan = dev.plan(state, ws)
+    try:
+        dev.tiled(tiles=[0, 1], state=state, plan=plan, finalize=False)
+        saved = state.clone()
+        dev.pda.pda_begin_step(plan, 2)
+        state.copy_(saved)
+        _, out = dev.tiled(tiles=[2, 3], state=state, plan=plan, begin=False)
+    finally:
+        dev.pda.pda_destroy(plan)
+    np.testing.assert_array_equal(state.cpu().numpy(), s_full.cpu().numpy())
+    np.testing.assert_array_equal(out_bits(out), out_bits(o_full))
+
+
+def test_poisoned_bytes_never_read():
+    """NaN in every byte outside the listed tokens (the case builder's default)
+    and a different value there give the same bits."""
+    announce("poison")
+    outs = []
+    for poison in (0x7FC0, 0x4000):
+        rng = np.random.Generator(np.random.PCG64(38))
+        case = build_case(rng, 3, 8, 2, 128, 16, [45, 3, 130], extra_pages=4, poison=poison, cap=12)
+        outs.append(out_bits(Device(case).decode()))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    assert np.all(np.isfinite(workloads.bf16_bits_to_f32(outs[0])))
+
+
+def test_tile_and_split_invariance():
+    announce("tile/split invariance")
+    rng = np.random.Generator(np.random.PCG64(39))
+    base = dict(S=3, Hq=16, Hkv=4, D=128, bs=16, contexts=[777, 300, 1024])
+    ref = None
+    for T in (1, 2, 4, 8):
+        r2 = np.random.Generator(np.random.PCG64(40))
+        case = build_case(r2, **base, n_tiles=T)
+        dev = Device(case)
+        if ref is None:
+            ref = oracle_of(dev)["out"]
+        _, out = dev.tiled()
+        assert_parity(out_to_f64(out), ref, label=f"T={T}")
+        if T == 1:
+            for bps in (1, 2, 7, 64):
+                assert_parity(out_to_f64(dev.decode(bps=bps)), ref, label=f"bps={bps}")
+
+
+def test_last_valid_scalar_default():
+    """A NULL last-valid array applies the scalar default to every sequence."""
+    announce("last-valid default")
+    rng = np.random.Generator(np.random.PCG64(41))
+    case = build_case(rng, 3, 8, 2, 64, 16, [21, 37, 53])     # all last pages hold 5 tokens
+    dev = Device(case)
+    a = out_bits(dev.decode(use_lastv_array=False, lv_default=5))
+    b = out_bits(dev.decode())
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_configs_sampled(cfg):
+    """The named workloads at full size, in the launch configuration the
+    benchmark times (automatic split size), checked on a sample of (sequence,
+    q head) pairs evaluated one by one by the oracle."""
+    announce("full config", cfg)
+    w = workloads.config(cfg)
+    dev = Device(w)
+    S, Hq = w.num_seqs, w.num_q_heads
+    rng = np.random.default_rng(cfg)
+    pairs = np.unique(np.concatenate([rng.choice(S * Hq, size=min(S * Hq, 96), replace=False),
+                                      [0, S * Hq - 1]]))
+    ref = oracle.attend_workload(w, pairs=pairs)
+    if len(w.tiles) == 1:
+        out = dev.decode()
+    else:
+        _, out = dev.tiled()
+    got = out_to_f64(out).reshape(S * Hq, w.head_dim)[pairs]
+    e = assert_parity(got, ref["out"], label=f"cfg{cfg}")
+    print(f"cfg{cfg} sampled max/mean err {e}")

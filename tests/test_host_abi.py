@@ -1,0 +1,211 @@
+"""Host-side checks of the C-ABI library: it loads, exports every declared
+symbol, and validates arguments before enqueuing anything (CPU only; no
+call here reaches a kernel)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import paged_gqa_decode_pda_amd as pda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pda.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(pda_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(pda.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    dyn = subprocess.run(["nm", "-D", "--defined-only", pda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", dyn, re.M), f"{n} not a defined text symbol"
+    assert sorted(pda.EXPORTED) == names
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HEADER}"\nint main(void){{pda_dims d={{1,1,1,8,1,1}};return (int)pda_dims_validate(&d);}}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-"],
+                       input=src, text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def dims(**kw):
+    base = dict(max_seqs=4, num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16,
+                tile_capacity=32)
+    base.update(kw)
+    return pda.pda_dims(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), pda.PDA_OK),
+    (dict(num_q_heads=6, num_kv_heads=4), pda.PDA_ERR_GQA),
+    (dict(head_dim=264), pda.PDA_ERR_HEAD_DIM),
+    (dict(head_dim=60), pda.PDA_ERR_HEAD_DIM),
+    (dict(head_dim=256), pda.PDA_OK),
+    (dict(head_dim=8), pda.PDA_OK),
+    (dict(max_seqs=0), pda.PDA_ERR_DIMS),
+    (dict(num_kv_heads=0), pda.PDA_ERR_DIMS),
+    (dict(block_size=0), pda.PDA_ERR_DIMS),
+    (dict(tile_capacity=0), pda.PDA_ERR_DIMS),
+    (dict(tile_capacity=1 << 21, block_size=16), pda.PDA_ERR_DIMS),
+    (dict(block_size=1), pda.PDA_OK),
+    (dict(num_q_heads=64, num_kv_heads=2), pda.PDA_OK),
+])
+def test_dims_validate(kw, status):
+    if status == pda.PDA_OK:
+        pda.pda_dims_validate(dims(**kw))
+    else:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_dims_validate(dims(**kw))
+        assert e.value.status == status
+        assert pda.pda_last_error()
+
+
+def test_page_constants_golden():
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    with pytest.raises(pda.PdaError):
+        pda.pda_dims_validate(dims(head_dim=g["max_head_dim"]["value"] + 8))
+    pda.pda_dims_validate(dims(head_dim=g["max_head_dim"]["value"]))
+
+
+def test_strides_golden():
+    g = json.load(open(os.path.join(GOLDEN, "strides.json")))
+    for c in g["cases"]:
+        d = pda.pda_dims(1, c["num_kv_heads"], c["num_kv_heads"], c["head_dim"], c["block_size"], 1)
+        if c["layout"] == "paged":
+            assert list(pda.pda_paged_strides(d)) == c["strides"]
+        else:
+            assert list(pda.pda_scratch_pool_strides(d)) == c["strides"]
+            assert pda.pda_scratch_pool_v_offset(d) == c["v_offset"]
+
+
+def test_state_and_workspace_sizes():
+    d = dims()
+    rows = 4 * 8
+    assert pda.pda_state_bytes(d) == rows * 4 * (2 + 64)
+    assert pda.pda_state_offsets(d) == (0, rows * 4, 2 * rows * 4)
+    for bps in (1, 3, 32, 100):
+        eff = min(bps, 32)
+        assert pda.pda_blocks_per_split(d, bps) == eff
+        assert pda.pda_workspace_bytes(d, bps) == rows * (-(-32 // eff)) * (64 + 2) * 4
+    auto = pda.pda_blocks_per_split(d, 0)
+    assert 1 <= auto <= 32
+    assert pda.pda_workspace_bytes(d, 0) >= pda.pda_workspace_bytes(d, auto)
+    big = dims(tile_capacity=4096)
+    assert pda.pda_blocks_per_split(big, 0) >= 4096 // 64
+    assert pda.pda_state_bytes(dims(num_q_heads=6, num_kv_heads=4)) == 0
+
+
+FAKE = 1 << 20          # a 16-byte aligned host-side address that is never dereferenced
+
+
+def test_decode_validation_before_enqueue():
+    d = dims()
+    st = (16 * 2 * 64, 2 * 64, 64)
+    args = dict(dims=d, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_tables=FAKE, block_counts=FAKE,
+                last_block_valid=None, last_block_valid_default=16, num_seqs=4, strides=st,
+                workspace=FAKE, out=FAKE, blocks_per_split=0, stream=0,
+                workspace_bytes=pda.pda_workspace_bytes(d))
+    cases = [
+        (dict(q=None), pda.PDA_ERR_NULL),
+        (dict(block_counts=None), pda.PDA_ERR_NULL),
+        (dict(out=None), pda.PDA_ERR_NULL),
+        (dict(q=FAKE + 2), pda.PDA_ERR_ALIGN),
+        (dict(k_pool=FAKE + 8), pda.PDA_ERR_ALIGN),
+        (dict(block_tables=FAKE + 2), pda.PDA_ERR_ALIGN),
+        (dict(out=FAKE + 4), pda.PDA_ERR_ALIGN),
+        (dict(strides=(st[0], st[1] + 4, st[2])), pda.PDA_ERR_ALIGN),
+        (dict(strides=(-st[0], st[1], st[2])), pda.PDA_ERR_ALIGN),
+        (dict(strides=(st[0], 1 << 30, st[2])), pda.PDA_ERR_DIMS),
+        (dict(num_seqs=5), pda.PDA_ERR_MAX_SEQS),
+        (dict(num_seqs=-1), pda.PDA_ERR_MAX_SEQS),
+        (dict(workspace_bytes=16), pda.PDA_ERR_WORKSPACE),
+        (dict(workspace=None, workspace_bytes=0), pda.PDA_ERR_WORKSPACE),
+        (dict(blocks_per_split=-1), pda.PDA_ERR_DIMS),
+        (dict(dims=dims(num_q_heads=6, num_kv_heads=4)), pda.PDA_ERR_GQA),
+    ]
+    for change, status in cases:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_decode(**{**args, **change})
+        assert e.value.status == status, (change, e.value)
+    # num_seqs == 0 is a valid no-op that enqueues nothing
+    pda.pda_decode(**{**args, "num_seqs": 0})
+
+
+def test_plan_validation_before_enqueue():
+    d = dims()
+    ws = pda.pda_workspace_bytes(d)
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_create(d, None, FAKE, 0, workspace_bytes=ws)
+    assert e.value.status == pda.PDA_ERR_NULL
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_create(d, FAKE, FAKE, 0, workspace_bytes=ws - 4)
+    assert e.value.status == pda.PDA_ERR_WORKSPACE
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_create(d, FAKE + 4, FAKE, 0, workspace_bytes=ws)
+    assert e.value.status == pda.PDA_ERR_ALIGN
+    plan = pda.pda_create(d, FAKE, FAKE, 0, workspace_bytes=ws)
+    try:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_begin_step(plan, 5, stream=0)
+        assert e.value.status == pda.PDA_ERR_MAX_SEQS
+        st = (16 * 2 * 64, 2 * 64, 64)
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_step_tile(plan, FAKE, FAKE, None, FAKE, FAKE, None, 16, 4, st, stream=0)
+        assert e.value.status == pda.PDA_ERR_NULL
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_step_tile(plan, FAKE, FAKE, FAKE, FAKE, FAKE, None, 16, 9, st, stream=0)
+        assert e.value.status == pda.PDA_ERR_MAX_SEQS
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_finalize(plan, None, 4, stream=0)
+        assert e.value.status == pda.PDA_ERR_NULL
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_finalize(plan, FAKE, 5, stream=0)
+        assert e.value.status == pda.PDA_ERR_MAX_SEQS
+        pda.pda_begin_step(plan, 0, stream=0)
+        pda.pda_finalize(plan, FAKE, 0, stream=0)
+    finally:
+        pda.pda_destroy(plan)
+
+
+def test_status_strings():
+    for i, n in enumerate(pda.STATUS_NAMES):
+        assert pda.pda_status_string(i) == n
+
+
+def test_missing_library_raises(tmp_path):
+    """Importing the binding without its library fails loudly; nothing falls back."""
+    import shutil
+    import sys
+    pkg = tmp_path / "paged_gqa_decode_pda_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "paged_gqa_decode_pda_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import paged_gqa_decode_pda_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "RuntimeError" in r.stderr and "missing" in r.stderr
+
+
+def test_split_count_limit():
+    """The split index is a grid dimension: more than 65535 splits per
+    sequence is rejected before anything is enqueued."""
+    d = dims(tile_capacity=1 << 17, block_size=1)
+    st = (1 * 2 * 64, 2 * 64, 64)
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, st, FAKE, FAKE, 1, stream=0,
+                       workspace_bytes=pda.pda_workspace_bytes(d, 1))
+    assert e.value.status == pda.PDA_ERR_DIMS
