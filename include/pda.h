@@ -101,13 +101,20 @@ pda_status pda_state_offsets(const pda_dims *dims, size_t offsets[3]);
 
 /* Pages per split-KV partition that a call with `blocks_per_split` uses:
  * the request clamped to [1, tile_capacity], or the library's own choice
- * when the request is 0 (never fewer than ceil(tile_capacity / 64) pages). */
+ * when the request is 0 (never fewer than ceil(tile_capacity / 256) pages). */
 int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
 
-/* Device workspace bytes for the split partials of max_seqs sequences with
- * the given blocks_per_split (0 = the library's choice, sized for any device):
- * max_seqs * num_q_heads * ceil(tile_capacity / bps) * (head_dim + 2) * 4.
- * 0 if dims are invalid. */
+/* Device workspace bytes for max_seqs sequences with the given
+ * blocks_per_split (0 = the library's choice, sized for any device): 256 bytes
+ * of control words (a work counter) followed by the fp32 split partials,
+ * max_seqs * num_q_heads * slots * (head_dim + 2) * 4, where slots is the
+ * most partial slots one sequence can need: at most ceil(tile_capacity / bps)
+ * (fewer when max_seqs <= 16384, since the kernel then groups most splits
+ * four at a time).
+ * The workspace must be zero-filled before its first use; every call that
+ * completes leaves the control words zero again, so a workspace is reused
+ * without clearing.  Calls that share a workspace must not run concurrently
+ * (order them on one stream).  0 if dims are invalid. */
 size_t pda_workspace_bytes(const pda_dims *dims, int32_t blocks_per_split);
 
 /* ([TA] paged_strides) layout [num_blocks, block_size, num_kv_heads, head_dim]:
@@ -124,7 +131,8 @@ int64_t pda_scratch_pool_v_offset(const pda_dims *dims);
 /* Creates a plan over caller-owned device buffers ([TA] TiledAttention::new,
  * which allocates its own state; here the caller does):
  *   state      device, pda_state_bytes(dims) bytes
- *   workspace  device, at least pda_workspace_bytes(dims, blocks_per_split)
+ *   workspace  device, at least pda_workspace_bytes(dims, blocks_per_split),
+ *              zero-filled before its first use
  *   blocks_per_split  0 = the library's choice
  * The buffers must outlive the plan.  *out receives the handle. */
 pda_status pda_create(const pda_dims *dims, void *state, void *workspace, size_t workspace_bytes,
@@ -160,11 +168,13 @@ pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, cons
  * ([TA] finalize).  out: device bf16 [num_seqs, num_q_heads, head_dim]. */
 pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *stream);
 
-/* One-shot decode: reset, one tile, finalize in two launches, with the
- * split partials in `workspace` ([CK] Overview: paged decode, split-KV).
+/* One-shot decode: split-KV partials, their log-sum-exp merge and o / l to
+ * bf16, with the split partials in `workspace` ([CK] Overview: paged decode,
+ * split-KV).
  * Arguments as pda_step_tile plus:
  *   dims        as for pda_create (num_seqs <= dims->max_seqs)
- *   workspace   device, at least pda_workspace_bytes(dims, blocks_per_split)
+ *   workspace   device, at least pda_workspace_bytes(dims, blocks_per_split),
+ *               zero-filled before its first use
  *   out         device bf16 [num_seqs, num_q_heads, head_dim]
  * A sequence with no token gets an all-zero output row. */
 pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,

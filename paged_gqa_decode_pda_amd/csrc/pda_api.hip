@@ -63,7 +63,7 @@ pda_status check_dims(const pda_dims *d) {
 }
 
 int32_t min_auto_bps(const pda_dims *d) {
-    const int32_t lo = (int32_t)ceil_div(d->tile_capacity, 64);
+    const int32_t lo = (int32_t)ceil_div(d->tile_capacity, 256);
     return lo < 1 ? 1 : lo;
 }
 
@@ -76,27 +76,48 @@ int device_cus() {
 }
 
 // Pages per split.  An explicit request is clamped to [1, tile_capacity].
-// Otherwise: the smallest power-of-two multiple of 8 pages (never below
-// ceil(cap / 64)) for which the workgroups of full-length sequences would
-// number at least 4 per compute unit, capped at the tile capacity.
+// Otherwise tile_capacity / 128 rounded to a power of two and clamped to
+// [8, 64] pages (never below ceil(tile_capacity / 256)): long page lists get
+// longer splits, so that a sequence's split count, and with it the combine
+// work, stays bounded.
 int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
+    (void)num_seqs;
     const int32_t cap = d->tile_capacity;
     if (request > 0) return request > cap ? cap : request;
-    const int32_t lo = min_auto_bps(d);
-    const int64_t G = d->num_q_heads / d->num_kv_heads;
-    const pda::Plan p = pda::choose_plan((int)G, d->head_dim, d->block_size);
-    const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * d->num_kv_heads * p.nhc;
-    const int64_t target = 4 * (int64_t)device_cus();
     int32_t bps = 8;
-    while (bps < cap && units * ceil_div(cap, bps) > target && bps < 64) bps *= 2;
-    if (bps < lo) bps = lo;
+    while (bps < 64 && bps * 128 < cap) bps *= 2;
+    if (bps < min_auto_bps(d)) bps = min_auto_bps(d);
     if (bps > cap) bps = cap;
     return bps;
 }
 
-size_t workspace_for(const pda_dims *d, int32_t bps, int64_t seqs) {
-    const int64_t nsplit = ceil_div(d->tile_capacity, bps);
-    return (size_t)seqs * d->num_q_heads * nsplit * (d->head_dim + 2) * sizeof(float);
+// Partial slots per sequence for splits of bps pages.  Up to kPrefixMaxSeqs
+// sequences the kernel groups about 3/4 of a sequence's splits four at a
+// time, so a sequence with n splits has n - 3 * floor(3n / 16) slots;
+// beyond that every split has its own slot.
+int64_t slots_per_seq(const pda_dims *d, int32_t bps) {
+    const int64_t nsp = ceil_div(d->tile_capacity, bps);
+    if (d->max_seqs > pda::kPrefixMaxSeqs) return nsp;
+    int64_t best = 1;
+    for (int64_t n = 1; n <= nsp; ++n) {
+        const int64_t slots = n - 3 * ((3 * n) / 16);
+        if (slots > best) best = slots;
+    }
+    return best;
+}
+
+int64_t units_of(const pda_dims *d) {
+    const int G = d->num_q_heads / d->num_kv_heads;
+    return (int64_t)d->num_kv_heads * pda::choose_plan(G, d->head_dim, d->block_size).nhc;
+}
+
+// Control words (int32), then split partials for max_seqs sequences:
+// (m, l) pairs, then o rows.
+size_t control_ints(const pda_dims *) { return (size_t)pda::kCtrlInts; }
+
+size_t workspace_for(const pda_dims *d, int32_t bps) {
+    return control_ints(d) * sizeof(int32_t) +
+           (size_t)d->max_seqs * d->num_q_heads * slots_per_seq(d, bps) * (d->head_dim + 2) * sizeof(float);
 }
 
 pda_status check_strides(const pda_dims *d, pda_strides st) {
@@ -122,11 +143,11 @@ pda_status check_tile_ptrs(const void *q, const void *k, const void *v, const in
     return PDA_OK;
 }
 
-pda::PartialArgs partial_args(const pda_dims *d, const void *q, const void *k, const void *v,
-                              const int32_t *blocks, const int32_t *counts, const int32_t *lastv,
-                              int32_t lv_default, pda_strides st, int32_t bps, void *ws, int S,
-                              const pda::Plan &p) {
-    pda::PartialArgs a;
+pda::AttendArgs attend_args(const pda_dims *d, const void *q, const void *k, const void *v,
+                            const int32_t *blocks, const int32_t *counts, const int32_t *lastv,
+                            int32_t lv_default, pda_strides st, int32_t bps, void *ws, int S,
+                            const pda::Plan &p) {
+    pda::AttendArgs a;
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
     a.v = static_cast<const uint16_t *>(v);
@@ -137,6 +158,7 @@ pda::PartialArgs partial_args(const pda_dims *d, const void *q, const void *k, c
     a.tok = st.tok;
     a.kvh = st.kvh;
     a.bs_magic = ((uint64_t(1) << 32) + (uint64_t)d->block_size - 1) / (uint64_t)d->block_size;
+    a.S = S;
     a.Hq = d->num_q_heads;
     a.Hkv = d->num_kv_heads;
     a.G = d->num_q_heads / d->num_kv_heads;
@@ -145,32 +167,18 @@ pda::PartialArgs partial_args(const pda_dims *d, const void *q, const void *k, c
     a.cap = d->tile_capacity;
     a.bps = bps;
     a.nhc = p.nhc;
-    a.nsplit = (int32_t)ceil_div(d->tile_capacity, bps);
+    a.nsplit = (int32_t)slots_per_seq(d, bps);   // partial slots per (sequence, q head)
     a.lv_default = lv_default;
+    a.prefix_mode = S <= pda::kPrefixMaxSeqs ? 1 : 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
-    float *wsf = static_cast<float *>(ws);
-    a.part_o = wsf;
-    a.part_ml = wsf + (int64_t)S * d->num_q_heads * a.nsplit * d->head_dim;
+    int32_t *wsi = static_cast<int32_t *>(ws);
+    a.ctrl = wsi;
+    float *wsf = reinterpret_cast<float *>(wsi + control_ints(d));
+    a.part_ml = wsf;
+    a.part_o = wsf + (int64_t)d->max_seqs * d->num_q_heads * a.nsplit * 2;
+    a.out = nullptr;
+    a.m = a.l = a.o = nullptr;
     return a;
-}
-
-pda::CombineArgs combine_args(const pda::PartialArgs &pa, int S) {
-    pda::CombineArgs c;
-    c.counts = pa.counts;
-    c.lastv = pa.lastv;
-    c.part_ml = pa.part_ml;
-    c.part_o = pa.part_o;
-    c.m = c.l = c.o = nullptr;
-    c.out = nullptr;
-    c.S = S;
-    c.Hq = pa.Hq;
-    c.D = pa.D;
-    c.bs = pa.bs;
-    c.cap = pa.cap;
-    c.bps = pa.bps;
-    c.nsplit = pa.nsplit;
-    c.lv_default = pa.lv_default;
-    return c;
 }
 
 pda_status hip_fail(hipError_t e, const char *what) {
@@ -213,7 +221,7 @@ size_t pda_workspace_bytes(const pda_dims *d, int32_t request) {
     if (check_dims(d) != PDA_OK) return 0;
     const int32_t bps = request > 0 ? (request > d->tile_capacity ? d->tile_capacity : request)
                                     : min_auto_bps(d);
-    return workspace_for(d, bps, d->max_seqs);
+    return workspace_for(d, bps);
 }
 
 pda_strides pda_paged_strides(const pda_dims *d) {
@@ -296,24 +304,18 @@ pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, cons
     if ((st = check_strides(d, strides)) != PDA_OK) return st;
     if (num_seqs == 0) return PDA_OK;
     const int32_t bps = resolve_bps(d, plan->bps_request, num_seqs);
-    if (ceil_div(d->tile_capacity, bps) > 65535)
-        return fail(PDA_ERR_DIMS, "more than 65535 splits per sequence; raise blocks_per_split");
-    if (workspace_for(d, bps, num_seqs) > plan->workspace_bytes)
-        return fail(PDA_ERR_WORKSPACE, "workspace too small for %d sequences", num_seqs);
+    if (workspace_for(d, bps) > plan->workspace_bytes)
+        return fail(PDA_ERR_WORKSPACE, "workspace too small");
     const int G = d->num_q_heads / d->num_kv_heads;
     const pda::Plan p = pda::choose_plan(G, d->head_dim, d->block_size);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    pda::PartialArgs a = partial_args(d, q, k_pool, v_pool, tile_blocks, tile_block_counts,
-                                      last_block_valid, last_block_valid_default, strides, bps,
-                                      plan->workspace, num_seqs, p);
-    hipError_t e = pda::launch_partial(p, a, num_seqs, hs);
-    if (e != hipSuccess) return hip_fail(e, "partial launch");
-    pda::CombineArgs c = combine_args(a, num_seqs);
-    c.m = plan->m;
-    c.l = plan->l;
-    c.o = plan->o;
-    e = pda::launch_combine(c, p.dp, hs);
-    return e == hipSuccess ? PDA_OK : hip_fail(e, "merge launch");
+    pda::AttendArgs a = attend_args(d, q, k_pool, v_pool, tile_blocks, tile_block_counts,
+                                    last_block_valid, last_block_valid_default, strides, bps,
+                                    plan->workspace, num_seqs, p);
+    a.m = plan->m;
+    a.l = plan->l;
+    a.o = plan->o;
+    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "tile launch");
 }
 
 pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *stream) {
@@ -351,23 +353,17 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
         return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
     if (num_seqs == 0) return PDA_OK;
     const int32_t bps = resolve_bps(dims, blocks_per_split, num_seqs);
-    if (ceil_div(dims->tile_capacity, bps) > 65535)
-        return fail(PDA_ERR_DIMS, "more than 65535 splits per sequence; raise blocks_per_split");
-    const size_t need = workspace_for(dims, bps, num_seqs);
+    const size_t need = workspace_for(dims, bps);
     if (!workspace || workspace_bytes < need)
         return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
     const int G = dims->num_q_heads / dims->num_kv_heads;
     const pda::Plan p = pda::choose_plan(G, dims->head_dim, dims->block_size);
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    pda::PartialArgs a = partial_args(dims, q, k_pool, v_pool, block_tables, block_counts,
-                                      last_block_valid, last_block_valid_default, strides, bps,
-                                      workspace, num_seqs, p);
-    hipError_t e = pda::launch_partial(p, a, num_seqs, hs);
-    if (e != hipSuccess) return hip_fail(e, "partial launch");
-    pda::CombineArgs c = combine_args(a, num_seqs);
-    c.out = static_cast<uint16_t *>(out);
-    e = pda::launch_combine(c, p.dp, hs);
-    return e == hipSuccess ? PDA_OK : hip_fail(e, "combine launch");
+    pda::AttendArgs a = attend_args(dims, q, k_pool, v_pool, block_tables, block_counts,
+                                    last_block_valid, last_block_valid_default, strides, bps,
+                                    workspace, num_seqs, p);
+    a.out = static_cast<uint16_t *>(out);
+    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "decode launch");
 }
 
 const char *pda_status_string(pda_status s) {

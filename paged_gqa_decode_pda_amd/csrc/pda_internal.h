@@ -7,45 +7,51 @@
 
 namespace pda {
 
-// Everything the split-KV partial kernel needs, passed by value.
-struct PartialArgs {
+// Layout of the caller's workspace, in this order:
+//   ctrl      64 int32: [0] next work item, [1] finished waves
+//   part_ml   fp32 [max_seqs, Hq, nsplit, 2]: (m in log2 units, l) per split
+//   part_o    fp32 [max_seqs, Hq, nsplit, D]
+// ctrl must be zero before a launch; every launch that completes leaves it
+// zero again.
+constexpr int kCtrlInts = 64;
+
+// Everything the attention kernel needs, passed by value.
+struct AttendArgs {
     const uint16_t *q;        // bf16 [S, Hq, D]
     const uint16_t *k;        // bf16 K pool base
     const uint16_t *v;        // bf16 V pool base
     const int32_t *blocks;    // int32 [S, cap] page ids
     const int32_t *counts;    // int32 [S]
     const int32_t *lastv;     // int32 [S] or null
-    float *part_ml;           // fp32 [S, Hq, nsplit, 2]: (m in log2 units, l)
-    float *part_o;            // fp32 [S, Hq, nsplit, D]
+    int32_t *ctrl;            // workspace control words
+    float *part_ml;           // workspace partials
+    float *part_o;
+    uint16_t *out;            // bf16 [S, Hq, D] (decode) or null
+    float *m, *l, *o;         // running state (tile) or null
     int64_t blk, tok, kvh;    // strides in bf16 elements
     uint64_t bs_magic;        // ceil(2^32 / bs): t / bs == (t * bs_magic) >> 32 for t < 2^24
-    int32_t Hq, Hkv, G, D, bs, cap, bps, nhc, nsplit, lv_default;
+    int32_t S, Hq, Hkv, G, D, bs, cap, bps, nhc, nsplit, lv_default;
+    int32_t prefix_mode;      // 1: enumerate only non-empty splits (needs 2 (S + 1) ints of LDS)
     float scale_log2;         // log2(e) / sqrt(D)
-};
-
-// Merge of split partials: into the output (decode) or into the state (tile).
-struct CombineArgs {
-    const int32_t *counts;
-    const int32_t *lastv;
-    const float *part_ml;
-    const float *part_o;
-    float *m, *l, *o;         // state (tile merge) or null
-    uint16_t *out;            // bf16 output (decode) or null
-    int32_t S, Hq, D, bs, cap, bps, nsplit, lv_default;
 };
 
 // Choices the host makes before launching.
 struct Plan {
     int dp;     // padded head dim: 64, 128 or 256
-    int gc;     // q heads per workgroup: 1, 2, 4 or 8
+    int gc;     // q heads per work item: 1, 2, 4 or 8
     int nhc;    // head chunks per kv head: ceil(G / gc)
     bool p16;   // block_size % 16 == 0: every 16-token group lies inside one page
 };
 
 Plan choose_plan(int G, int D, int bs);
 
-hipError_t launch_partial(const Plan &p, const PartialArgs &a, int S, hipStream_t st);
-hipError_t launch_combine(const CombineArgs &a, int dp, hipStream_t st);
+// Sequences up to this count enumerate work items through an LDS prefix sum.
+constexpr int kPrefixMaxSeqs = 16384;
+
+// Launches the persistent attention kernel and, when sequences may have
+// several splits, the combine kernel (decode when a.out is set, else a tile
+// folded into the running state).  `cus` is the device's compute-unit count.
+hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st);
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st);
 hipError_t launch_finalize(const float *l, const float *o, uint16_t *out, int64_t rows, int D,
                            hipStream_t st);

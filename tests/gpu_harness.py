@@ -93,7 +93,8 @@ class Device:
 
     def workspace(self, bps=0):
         n = self.pda.pda_workspace_bytes(self.dims(), bps)
-        return self.torch.empty(max(1, n // 4), dtype=self.torch.float32, device=self.dev)
+        # zero-filled before first use, as the library requires
+        return self.torch.zeros(max(1, n // 4), dtype=self.torch.float32, device=self.dev)
 
     def new_out(self, fill=None):
         t = self.torch.empty(self.max_seqs, self.p.Hq, self.p.D, dtype=self.torch.int16,
