@@ -19,7 +19,10 @@ ARCH = "gfx950"
 # host pass warns that it does not know the feature, which is harmless.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
+             "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
+             # single-lane work-queue claims: keep the compiler from turning
+             # them into wave reductions that read the result back at once
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def hipcc() -> str:

@@ -22,13 +22,14 @@
 //   reset_kernel / finalize_kernel  state fill and o / l -> bf16.
 //
 // Lane layouts of a wave (D_PAD = padded head dim, 64/128/256):
-//   K: 4 lanes per token, 16 tokens per wave; lane (t = lane/4, j = lane%4)
-//      holds the 16-byte chunks 4c + j (c < D_PAD/32) of token t's K row, so
-//      each load instruction reads 64 contiguous bytes of 16 rows.  Scores use
-//      v_dot2c_f32_bf16 on bf16 pairs and a 2-step quad DPP reduction.
+//   q, K: operands of v_mfma_f32_16x16x32_bf16 (16 heads x 16 tokens per
+//      instruction, 32 elements of the head dim deep).  Lane l holds the
+//      16-byte chunk 32c + 8(l/16) of head l%16 (q) and of token l%16 (K), so
+//      each K load instruction reads 64 contiguous bytes of 16 rows.  The
+//      scores come back with lane = token and heads 4(l/16) + i.
 //   V: 16 lanes per token row, 4 rows per wave; lane (r = lane/16, c =
 //      lane%16) holds elements [c*D_PAD/16, (c+1)*D_PAD/16) of token 4i + r.
-//      Softmax weights move from the K layout to the V layout through LDS.
+//      Softmax weights move from the score layout to the V layout through LDS.
 #include "pda_internal.h"
 
 #include <map>
@@ -40,7 +41,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -48,18 +48,11 @@ constexpr int kWaves = 4;
 constexpr int kBigSplits = 4;   // splits per big work item
 constexpr int kThreads = 64 * kWaves;
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 // The two bf16 halves of a dword, widened exactly to fp32.
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 // DPP lane permutations (all source lanes valid for the controls used).
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;   // row_ror:4 (within 16-lane rows)
 constexpr int kRowRor8 = 0x128;   // row_ror:8
 
@@ -72,22 +65,13 @@ __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x,
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Split partials travel between workgroups (possibly on different XCDs, each
-// with its own L2) through device-coherent accesses: agent-scope relaxed
-// atomic stores and loads, which gfx950 issues with sc1 (written through to,
-// and read from, the device coherence point).  No L2 writeback or invalidate
-// is needed; a writer only waits for its stores to complete before counting
-// its split in.
-__device__ __forceinline__ void st_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// The work counter is rewound with an agent-scope store (gfx950: sc1, written
+// through to the device coherence point) so that the next launch, on any XCD,
+// sees it.
 __device__ __forceinline__ void st_coherent_i(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0): this wave's loads and stores completed
+constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0): this wave's vector memory operations completed
 
 // Lanes of one wave exchange data through LDS: make prior LDS writes visible
 // to the wave's other lanes before the reads that follow.
@@ -109,6 +93,44 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
 
+// VE / 2 dwords of bf16 pairs (VE = 2 or 4 elements).
+template <int VE>
+__device__ __forceinline__ void ld_v(const uint16_t *p, uint32_t (&r)[VE / 2]) {
+    if constexpr (VE == 2) {
+        r[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        const u32x2 x = ld8(p);
+        r[0] = x[0];
+        r[1] = x[1];
+    }
+}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void ld_f(const float *p, float (&t)[N]) {
+    if constexpr (N == 2) {
+        const f32x2 x = *reinterpret_cast<const f32x2 *>(p);
+        t[0] = x[0];
+        t[1] = x[1];
+    } else {
+        const f32x4v x = *reinterpret_cast<const f32x4v *>(p);
+        t[0] = x[0];
+        t[1] = x[1];
+        t[2] = x[2];
+        t[3] = x[3];
+    }
+}
+template <int N>
+__device__ __forceinline__ void st_f(float *p, const float (&t)[N]) {
+    if constexpr (N == 2) *reinterpret_cast<f32x2 *>(p) = f32x2{t[0], t[1]};
+    else *reinterpret_cast<f32x4v *>(p) = f32x4v{t[0], t[1], t[2], t[3]};
+}
+template <int N>
+__device__ __forceinline__ void st_u(uint16_t *p, const uint32_t (&t)[N]) {
+    if constexpr (N == 1) *reinterpret_cast<uint32_t *>(p) = t[0];
+    else *reinterpret_cast<u32x2 *>(p) = u32x2{t[0], t[1]};
+}
+
 // Tokens of sequence s: the first `cnt` listed pages, all full except the
 // last, which holds `lv` valid slots.
 __device__ __forceinline__ int seq_tokens(const int32_t *counts, const int32_t *lastv, int lv_default,
@@ -123,13 +145,25 @@ __device__ __forceinline__ int page_of(uint32_t t, uint64_t magic) {
     return (int)(((uint64_t)t * magic) >> 32);
 }
 
-// Per-wave registers of one 16-token group.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// V lane layout: a row step covers VR token rows, VL lanes per row, VE
+// consecutive elements per lane (one dword or two), so each load instruction
+// reads whole rows and every lane accumulates its own elements.
+template <int DP>
+struct VLayout {
+    static constexpr int VE = DP == 256 ? 4 : 2;
+    static constexpr int VL = DP / VE;   // 32, 64, 64
+    static constexpr int VR = 64 / VL;   // 2, 1, 1
+    static constexpr int NS = 16 / VR;   // row steps per 16-token group
+};
+
+// Registers of one 16-token group in flight.
 template <int DP>
 struct GroupRegs {
-    static constexpr int NCK = DP / 32;   // 16-byte K chunks per lane
-    static constexpr int VW = DP / 32;    // V dwords per lane per row step (DP/16 bf16)
-    u32x4 k[NCK];
-    uint32_t v[4][VW];
+    u32x4 k[DP / 32];   // K, MFMA B-operand layout: token lane % 16, elements 32 c + 8 (lane / 16) .. + 8
+    uint32_t v[VLayout<DP>::NS][VLayout<DP>::VE / 2];   // V: token VR i + lane / VL, elements VE (lane % VL) .. + VE
 };
 
 __device__ __forceinline__ int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
@@ -137,267 +171,21 @@ __device__ __forceinline__ float readlanef(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// Maximum over the 64 lanes of a value that is already equal within each
-// 16-lane row: four lane reads, result in a scalar register.
-__device__ __forceinline__ float row_values_max(float x) {
-    return fmaxf(fmaxf(readlanef(x, 0), readlanef(x, 16)), fmaxf(readlanef(x, 32), readlanef(x, 48)));
+constexpr int kRowRor1 = 0x121;   // row_ror:1
+constexpr int kRowRor2 = 0x122;   // row_ror:2
+
+// Maximum / sum over each 16-lane row, left in every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<kRowRor8>(x));
+    x = fmaxf(x, dpp<kRowRor4>(x));
+    x = fmaxf(x, dpp<kRowRor2>(x));
+    return fmaxf(x, dpp<kRowRor1>(x));
 }
-
-// Per-wave shared memory.
-template <int GC>
-struct WaveSmem {
-    float p[16][GC];       // softmax weights, K lane layout -> V lane layout
-    float wt[GC][64];      // merge: weights of one 64-split chunk
-};
-
-// One wave streams the 16-token groups of the token range [t0, t1) of
-// sequence s for kv head g and the q heads h0 .. h0 + nh - 1, NBUF groups of
-// K/V in flight in registers while it computes.  The page ids are read once
-// per 64 pages into one VGPR (lane i holds page cb + i of the sequence's list)
-// and picked with readlane (pages of 16k tokens) or a lane shuffle (other
-// block sizes), so no table load sits between a group's address and its data.
-// On return m2 (log2 units), lsum and acc_o hold the wave's totals in every
-// lane: acc_o[h][e] is element col * DP/16 + e of head h.
-template <int DP, int GC, bool P16, int NBUF>
-__device__ __forceinline__ void wave_pass(const AttendArgs &a, WaveSmem<GC> &ws, int lane, int s,
-                                          int g, int h0, int nh, int t0, int t1, int cnt,
-                                          float (&m2)[GC], float (&lsum)[GC],
-                                          float (&acc_o)[GC][DP / 16]) {
-    constexpr int NCK = DP / 32;
-    constexpr int VW = DP / 32;      // V dwords per lane per row step
-    constexpr int VPL = DP / 16;     // V elements per lane
-    constexpr int VC = DP == 64 ? 1 : VW / 4;
-
-    const int ngroups = (t1 - t0 + 15) >> 4;
-    const int32_t *brow = a.blocks + (int64_t)s * a.cap;
-    const int quad = lane >> 2, ql = lane & 3;
-    const int row = lane >> 4, col = lane & 15;
-
-    // Lane-invariant element offsets.  Chunks past head_dim re-read chunk 0
-    // of the same row (in bounds); q is zero there, and V lanes past head_dim
-    // are never stored.
-    int kd[NCK];
-#pragma unroll
-    for (int c = 0; c < NCK; ++c) {
-        const int d0 = 8 * (4 * c + ql);
-        kd[c] = d0 < a.D ? d0 : 0;
-    }
-    int vd[VC];
-#pragma unroll
-    for (int c = 0; c < VC; ++c) {
-        const int e0 = col * VPL + 8 * c;
-        vd[c] = e0 < a.D ? e0 : 0;
-    }
-    const int tok32 = (int)a.tok;
-    const int64_t gk = (int64_t)g * a.kvh;
-
-    // q chunks in the K lane layout, zero past head_dim.  Padding heads of a
-    // short last head chunk (h >= nh) repeat head nh - 1; their results are
-    // never stored.
-    u32x4 qr[GC][NCK];
-#pragma unroll
-    for (int h = 0; h < GC; ++h) {
-        const uint16_t *qp = a.q + ((int64_t)s * a.Hq + h0 + min(h, nh - 1)) * a.D;
-#pragma unroll
-        for (int c = 0; c < NCK; ++c) {
-            const u32x4 x = ld16(qp + kd[c]);
-            qr[h][c] = 8 * (4 * c + ql) < a.D ? x : u32x4{0, 0, 0, 0};
-        }
-    }
-
-#pragma unroll
-    for (int h = 0; h < GC; ++h) {
-        m2[h] = -INFINITY;
-        lsum[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) acc_o[h][e] = 0.f;
-    }
-
-    int cb = 0, bidvec = 0;   // page-id window: lane i holds brow[cb + i]
-    auto load_window = [&](int first) {
-        cb = first;
-        bidvec = brow[min(first + lane, cnt - 1)];
-    };
-
-    auto issue = [&](int n, GroupRegs<DP> &r) {
-        const int gs = t0 + 16 * n;
-        if constexpr (P16) {
-            const int page = page_of((uint32_t)gs, a.bs_magic);
-            const int bid = readlane(bidvec, page - cb);
-            const int64_t off = (int64_t)bid * a.blk + gk + (int64_t)(gs - page * a.bs) * a.tok;
-            const uint16_t *kb = a.k + off;
-            const uint16_t *vb = a.v + off;
-#pragma unroll
-            for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kb + (quad * tok32 + kd[c]));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ro = (4 * i + row) * tok32;
-                if constexpr (DP == 64) {
-                    const u32x2 x = ld8(vb + (ro + vd[0]));
-                    r.v[i][0] = x[0];
-                    r.v[i][1] = x[1];
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VC; ++c) {
-                        const u32x4 x = ld16(vb + (ro + vd[c]));
-                        r.v[i][4 * c + 0] = x[0];
-                        r.v[i][4 * c + 1] = x[1];
-                        r.v[i][4 * c + 2] = x[2];
-                        r.v[i][4 * c + 3] = x[3];
-                    }
-                }
-            }
-        } else {
-            // tokens past t1 read the group's first token instead (in bounds)
-            const int tk = gs + quad < t1 ? gs + quad : gs;
-            const int pk = page_of((uint32_t)tk, a.bs_magic);
-            const int bk = __shfl(bidvec, pk - cb, 64);
-            const uint16_t *kp = a.k + ((int64_t)bk * a.blk + gk + (int64_t)(tk - pk * a.bs) * a.tok);
-#pragma unroll
-            for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kp + kd[c]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tv = gs + 4 * i + row < t1 ? gs + 4 * i + row : gs;
-                const int pv = page_of((uint32_t)tv, a.bs_magic);
-                const int bv = __shfl(bidvec, pv - cb, 64);
-                const uint16_t *vp = a.v + ((int64_t)bv * a.blk + gk + (int64_t)(tv - pv * a.bs) * a.tok);
-                if constexpr (DP == 64) {
-                    const u32x2 x = ld8(vp + vd[0]);
-                    r.v[i][0] = x[0];
-                    r.v[i][1] = x[1];
-                } else {
-#pragma unroll
-                    for (int c = 0; c < VC; ++c) {
-                        const u32x4 x = ld16(vp + vd[c]);
-                        r.v[i][4 * c + 0] = x[0];
-                        r.v[i][4 * c + 1] = x[1];
-                        r.v[i][4 * c + 2] = x[2];
-                        r.v[i][4 * c + 3] = x[3];
-                    }
-                }
-            }
-        }
-    };
-
-    auto compute = [&](GroupRegs<DP> &r, int n) {
-        const int gs = t0 + 16 * n;
-        // scores of token gs + quad for every head of the chunk
-        float acc[GC];
-#pragma unroll
-        for (int h = 0; h < GC; ++h) {
-            float x = 0.f;
-#pragma unroll
-            for (int c = 0; c < NCK; ++c) {
-                x = dot2(qr[h][c][0], r.k[c][0], x);
-                x = dot2(qr[h][c][1], r.k[c][1], x);
-                x = dot2(qr[h][c][2], r.k[c][2], x);
-                x = dot2(qr[h][c][3], r.k[c][3], x);
-            }
-            x += dpp<kQuadSwap1>(x);
-            x += dpp<kQuadSwap2>(x);
-            acc[h] = x;
-        }
-        const bool valid = gs + quad < t1;
-        float sc[GC];
-        bool grow = false;
-        float alpha[GC];
-#pragma unroll
-        for (int h = 0; h < GC; ++h) {
-            sc[h] = valid ? acc[h] * a.scale_log2 : -INFINITY;
-            float x = sc[h];
-            x = fmaxf(x, dpp<kRowRor4>(x));
-            x = fmaxf(x, dpp<kRowRor8>(x));
-            const float mn = fmaxf(m2[h], row_values_max(x));
-            grow |= mn > m2[h];
-            alpha[h] = (mn == -INFINITY) ? 1.f : exp2_fast(m2[h] - mn);
-            m2[h] = mn;
-        }
-        if (grow) {  // uniform: m2 is identical in every lane
-#pragma unroll
-            for (int h = 0; h < GC; ++h) {
-                lsum[h] *= alpha[h];
-#pragma unroll
-                for (int e = 0; e < VPL; ++e) acc_o[h][e] *= alpha[h];
-            }
-        }
-        float p[GC];
-#pragma unroll
-        for (int h = 0; h < GC; ++h) {
-            p[h] = valid ? exp2_fast(sc[h] - m2[h]) : 0.f;
-            lsum[h] += p[h];
-        }
-        if (ql == 0) {
-#pragma unroll
-            for (int h = 0; h < GC; ++h) ws.p[quad][h] = p[h];
-        }
-        // the last group of a range may hold tokens past t1: zero their V so
-        // that 0 * (NaN or Inf) never reaches the sums
-        if (gs + 16 > t1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = gs + 4 * i + row < t1;
-#pragma unroll
-                for (int e = 0; e < VW; ++e) r.v[i][e] = ok ? r.v[i][e] : 0u;
-            }
-        }
-        wave_lds_sync();
-        // o += p * V, token 4i + row per row step
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float pv[GC];
-#pragma unroll
-            for (int h = 0; h < GC; ++h) pv[h] = ws.p[4 * i + row][h];
-#pragma unroll
-            for (int e = 0; e < VW; ++e) {
-                const float f0 = bf_lo(r.v[i][e]);
-                const float f1 = bf_hi(r.v[i][e]);
-#pragma unroll
-                for (int h = 0; h < GC; ++h) {
-                    acc_o[h][2 * e] = fmaf(pv[h], f0, acc_o[h][2 * e]);
-                    acc_o[h][2 * e + 1] = fmaf(pv[h], f1, acc_o[h][2 * e + 1]);
-                }
-            }
-        }
-        wave_lds_sync();
-    };
-
-    // groups covered by one 64-page window
-    const int per_window = P16 ? 4 * a.bs : max(1, (62 * a.bs + 1) / 16);
-    for (int c0 = 0; c0 < ngroups; c0 += per_window) {
-        const int nc = min(per_window, ngroups - c0);
-        load_window(page_of((uint32_t)(t0 + 16 * c0), a.bs_magic));
-        // Loads are issued unconditionally (indices past the window re-read
-        // its last group, an L2 hit) so that every wait for a group's data
-        // counts exactly the younger loads; only the compute is skipped.
-        GroupRegs<DP> rb[NBUF];
-#pragma unroll
-        for (int j = 0; j < NBUF - 1; ++j) issue(c0 + min(j, nc - 1), rb[j]);
-        for (int n = 0; n < nc; n += NBUF) {
-#pragma unroll
-            for (int j = 0; j < NBUF; ++j) {
-                issue(c0 + min(n + j + NBUF - 1, nc - 1), rb[(j + NBUF - 1) % NBUF]);
-                if (n + j < nc) compute(rb[j], c0 + n + j);
-            }
-        }
-    }
-
-    // Wave totals in every lane: o over the 4 rows, l over the 16 token quads.
-#pragma unroll
-    for (int h = 0; h < GC; ++h) {
-#pragma unroll
-        for (int e = 0; e < VPL; ++e) {
-            float x = acc_o[h][e];
-            x += shfl_xor(x, 16);
-            x += shfl_xor(x, 32);
-            acc_o[h][e] = x;
-        }
-        float y = lsum[h];
-        y += shfl_xor(y, 4);
-        y += shfl_xor(y, 8);
-        y += shfl_xor(y, 16);
-        y += shfl_xor(y, 32);
-        lsum[h] = y;
-    }
+__device__ __forceinline__ float row_sum16(float x) {
+    x += dpp<kRowRor8>(x);
+    x += dpp<kRowRor4>(x);
+    x += dpp<kRowRor2>(x);
+    return x + dpp<kRowRor1>(x);
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -417,6 +205,13 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x + shfl_xor(x, 32);
 }
 
+// Softmax weights of one group, moving from the score layout (lane = token)
+// to the V layout (16 lanes per token row).
+template <int GC>
+struct WaveSmem {
+    float p[16][GC];
+};
+
 // Splits of a sequence: ceil(ntok / span), 0 for an empty sequence.
 __device__ __forceinline__ int splits_of(int ntok, int span) { return ntok > 0 ? (ntok + span - 1) / span : 0; }
 
@@ -430,16 +225,48 @@ __device__ __forceinline__ int slots_of(int nsp, bool prefix_mode) {
     return prefix_mode ? nsp - (kBigSplits - 1) * big_items_of(nsp) : nsp;
 }
 
+// One work item as a wave holds it.  Everything is wave-uniform except bidvec
+// and q.
+template <int DP>
+struct Item {
+    int kind;        // 0: attend tokens [t0, t1); 1: zero the decode output rows; 2: nothing
+    int s, g, h0, nh, split, nspl, slot;
+    int cnt, t0, t1, ng, nsp;
+    int cb;          // first page (index into the sequence's list) of the page-id window
+    int bidvec;      // the window: lane i holds the id of page cb + i
+    u32x4 q[DP / 32];  // MFMA A operand: head lane % 16, elements 32 c + 8 (lane / 16) .. + 8
+};
+
 // Persistent attention kernel.  Work items are (sequence, split, unit), unit =
-// (kv head, head chunk) fastest, and every wave takes items on its own from an
-// atomic counter, so the waves reading the interleaved kv-head rows of the
-// same pages run together and no wave ever waits for another.  A sequence
-// with one split gets its result written directly (bf16 o / l for decode, the
-// running state folded for a tile); otherwise every split leaves an (m, l, o)
-// partial in the workspace for combine_kernel.
+// (kv head, head chunk) fastest, so the waves reading the interleaved kv-head
+// rows of the same pages run together.  Every wave takes items from an atomic
+// counter on its own and never waits for another wave.
+//
+// A wave's items form one stream of 16-token groups with NBUF - 1 groups in
+// flight: the last ring slots of an item already load the next item's first
+// groups.  The next item is claimed three ring rounds before the end of the
+// current one, located and its counts, q rows and page ids requested two
+// rounds before, and resolved at the start of the last round, so every wait
+// lands on loads issued a round earlier and the stream does not drain between
+// items (items of fewer than three rounds take the next item synchronously).
+//
+// Per group: q.K^T as DP/32 v_mfma_f32_16x16x32_bf16 (A = the head chunk's q
+// rows, B = 16 K rows loaded straight into the operand layout, 64 contiguous
+// bytes of 16 rows per load); the scores land with lane = token and heads
+// 4 (lane / 16) + i in the four result registers.  A base-2 online softmax
+// per head uses 16-lane DPP maxima and a wave-uniform running max; the weights
+// move to the V layout through LDS and P.V accumulates in fp32 FMAs.  A
+// sequence with one split gets its result written directly (bf16 o / l for
+// decode, folded into the running state for a tile); otherwise every item
+// leaves an (m, l, o) partial in its slot for combine_kernel.
 template <int DP, int GC, bool P16, int NBUF, bool TILE>
 __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
-    constexpr int VPL = DP / 16;
+    constexpr int NCK = DP / 32;
+    constexpr int VE = VLayout<DP>::VE, VL = VLayout<DP>::VL, VR = VLayout<DP>::VR, NS = VLayout<DP>::NS;
+    constexpr int HR = (GC + 3) / 4;   // score rows (of 16 lanes) that hold real heads
+    constexpr int NI = GC < 4 ? GC : 4;
+    static_assert(GC <= 8 && NBUF >= 2, "at most 8 q heads per item, at least 2 ring slots");
+
     __shared__ WaveSmem<GC> wsm[kWaves];
     __shared__ int scan[2 * kWaves];
     extern __shared__ int prefix[];   // 2 (S + 1) ints when a.prefix_mode
@@ -460,6 +287,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     int nbig_pairs = 0, npairs;
     int *pbig = prefix;                 // big items before sequence s
     int *psmall = prefix + a.S + 1;     // small items before sequence s
+    const int nsp_max = (a.cap + a.bps - 1) / a.bps;
     if (a.prefix_mode) {
         int carry_b = 0, carry_s = 0;
         for (int base = 0; base < a.S; base += kThreads) {
@@ -506,21 +334,40 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
         nbig_pairs = __builtin_amdgcn_readfirstlane(carry_b);
         npairs = nbig_pairs + __builtin_amdgcn_readfirstlane(carry_s);
     } else {
-        npairs = a.S * ((a.cap + a.bps - 1) / a.bps);
+        npairs = a.S * nsp_max;
     }
     const int nitems = npairs * units;
     __syncthreads();
 
-    // Wave gw starts on item gw; later items come from the counter (which
-    // counts from the number of waves).  An item is claimed only when the
-    // previous one is done, so no item waits behind a busy wave.
     WaveSmem<GC> &ws = wsm[w];
     const int nwaves = (int)gridDim.x * kWaves;
-    int it = (int)blockIdx.x * kWaves + w;
-    while (it < nitems) {
+    const int tok32 = (int)a.tok;
+    // without per-sequence last-valid counts, any in-bounds int array stands in
+    // (its values are not used)
+    const int32_t *lv_src = a.lastv ? a.lastv : a.counts;
+
+    // Lane-invariant element offsets.  K chunks past head_dim re-read chunk 0
+    // of the same row (in bounds; q is zero there); V lanes past head_dim are
+    // never stored.
+    int kd[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+        const int d0 = 32 * c + 8 * row;
+        kd[c] = d0 < a.D ? d0 : 0;
+    }
+    const int vr = VR == 1 ? 0 : lane / VL;   // V row within a step
+    const int ve0 = (lane % VL) * VE;          // first V element of the lane
+    const bool vok = ve0 < a.D;                // head_dim is a multiple of 8: all VE elements in, or all out
+    const int vofs = vok ? ve0 : 0;
+    const int vlane = vr * (int)a.tok + vofs;
+
+    // Step 1 of taking item `it`: where it is, from LDS only.  An index past
+    // the last item becomes kind 2 with in-bounds coordinates.
+    auto locate = [&](int it, Item<DP> &x) {
+        x.kind = it < nitems ? 0 : 2;
+        if (it >= nitems) it = 0;
         int pair = it / units;
         const int unit = it - pair * units;
-        int s, split, nspl = 1, slot;   // first split, splits covered, partial slot
         if (a.prefix_mode) {
             const bool big = pair < nbig_pairs;
             const int *pf = big ? pbig : psmall;
@@ -531,100 +378,368 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
                 if (pf[mid] <= pair) lo = mid;
                 else hi = mid;
             }
-            s = __builtin_amdgcn_readfirstlane(lo);
-            const int j = pair - __builtin_amdgcn_readfirstlane(pf[s]);
+            x.s = __builtin_amdgcn_readfirstlane(lo);
+            const int j = pair - __builtin_amdgcn_readfirstlane(pf[x.s]);
             if (big) {
-                split = j * kBigSplits;
-                nspl = kBigSplits;
-                slot = j;
+                x.split = j * kBigSplits;
+                x.nspl = kBigSplits;
+                x.slot = j;
             } else {
-                const int nb_s = big_items_of(splits_of(seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs), span));
-                split = nb_s * kBigSplits + j;
-                slot = nb_s + j;
+                const int nb_s = __builtin_amdgcn_readfirstlane(pbig[x.s + 1] - pbig[x.s]);
+                x.split = nb_s * kBigSplits + j;
+                x.nspl = 1;
+                x.slot = nb_s + j;
             }
         } else {
-            const int nsp_max = (a.cap + a.bps - 1) / a.bps;
-            s = pair / nsp_max;
-            split = pair - s * nsp_max;
-            slot = split;
+            x.s = pair / nsp_max;
+            x.split = pair - x.s * nsp_max;
+            x.nspl = 1;
+            x.slot = x.split;
         }
-        const int g = unit / a.nhc;
-        const int hc = unit - g * a.nhc;
-        const int h0 = g * a.G + hc * GC;
-        const int nh = min(GC, a.G - hc * GC);
-        const int cnt = clampi(a.counts[s], 0, a.cap);
-        const int ntok = seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs);
-        const int nsp = splits_of(ntok, span);
-        const int64_t row0 = (int64_t)s * a.Hq + h0;   // first (sequence, q head) row
+        x.g = unit / a.nhc;
+        const int hc = unit - x.g * a.nhc;
+        x.h0 = x.g * a.G + hc * GC;
+        x.nh = min(GC, a.G - hc * GC);
+        x.cb = x.split * a.bps;   // the split's first page (< tile_capacity)
+    };
 
+    // Step 2: request the sequence's counts, the q rows and the page-id
+    // window (page ids past the list are read but never used).
+    auto fetch = [&](Item<DP> &x, int &cnt_raw, int &lv_raw) {
+        cnt_raw = a.counts[x.s];
+        lv_raw = lv_src[x.s];
+        const uint16_t *qp = a.q + ((int64_t)x.s * a.Hq + x.h0 + min(col, x.nh - 1)) * a.D;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) x.q[c] = ld16(qp + kd[c]);
+        x.bidvec = a.blocks[(int64_t)x.s * a.cap + min(x.cb + lane, a.cap - 1)];
+    };
+
+    // Step 3: the token range, from the counts.
+    auto resolve = [&](Item<DP> &x, int cnt_raw, int lv_raw) {
+        x.t0 = x.t1 = x.ng = 0;   // no token range unless it attends
+        x.cnt = clampi(__builtin_amdgcn_readfirstlane(cnt_raw), 0, a.cap);
+        const int lv = clampi(a.lastv ? __builtin_amdgcn_readfirstlane(lv_raw) : a.lv_default, 0, a.bs);
+        const int ntok = x.cnt > 0 ? (x.cnt - 1) * a.bs + lv : 0;
+        x.nsp = splits_of(ntok, span);
+#pragma unroll
+        for (int c = 0; c < NCK; ++c)
+            x.q[c] = (col < x.nh && 32 * c + 8 * row < a.D) ? x.q[c] : u32x4{0, 0, 0, 0};
+        if (x.kind != 0) return;
         if (ntok == 0) {
-            // only decode gets here (an empty sequence's single item): zero rows
-            if (!TILE && split == 0) {
-                for (int idx = lane; idx < nh * a.D; idx += 64) a.out[row0 * a.D + idx] = 0;
+            x.kind = (!TILE && (a.prefix_mode || x.split == 0)) ? 1 : 2;
+            return;
+        }
+        if (x.split >= x.nsp) {
+            x.kind = 2;
+            return;
+        }
+        x.t0 = x.split * span;
+        x.t1 = min(x.t0 + x.nspl * span, ntok);
+        x.ng = (x.t1 - x.t0 + 15) >> 4;
+    };
+
+    auto claim_next = [&]() {
+        const int grabbed = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
+        return nwaves + readlane(grabbed, 0);
+    };
+
+    // Takes items from `it` on until one has tokens or the queue is empty,
+    // writing the zero rows of empty decode sequences on the way.
+    auto take_sync = [&](int it, Item<DP> &x) {
+        for (;;) {
+            int cr, lr;
+            locate(it, x);
+            fetch(x, cr, lr);
+            // complete every request here, so that none is left pending into
+            // the ring loop
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            resolve(x, cr, lr);
+            if (x.kind == 0 || it >= nitems) return;
+            if (x.kind == 1) {
+                const int64_t row0 = (int64_t)x.s * a.Hq + x.h0;
+                for (int idx = lane; idx < x.nh * a.D; idx += 64) a.out[row0 * a.D + idx] = 0;
             }
-        } else if (split < nsp) {
-            const int t0 = split * span;
-            const int t1 = min(t0 + nspl * span, ntok);
-            float m2[GC], lsum[GC], acc_o[GC][VPL];
-            wave_pass<DP, GC, P16, NBUF>(a, ws, lane, s, g, h0, nh, t0, t1, cnt, m2, lsum, acc_o);
-            // row-0 lanes store elements e0 .. e0 + VPL - 1; with a padded
-            // head dim of 256 a lane's slice may straddle head_dim, so every
-            // element is checked
-            const int e0 = col * VPL;
-            const bool store = row == 0 && e0 < a.D;
-            if (nsp == 1) {
+            it = claim_next();
+        }
+    };
+
+    // Loads of group n of item x (indices past the last group re-read it: in
+    // bounds, never computed).
+    auto issue = [&](Item<DP> &x, int n, GroupRegs<DP> &r) {
+        n = min(n, x.ng - 1);
+        const int gs = x.t0 + 16 * n;
+        const int64_t gk = (int64_t)x.g * a.kvh;
+        const int32_t *brow = a.blocks + (int64_t)x.s * a.cap;
+        if constexpr (P16) {
+            const int page = page_of((uint32_t)gs, a.bs_magic);
+            if (page - x.cb >= 64) {   // move the window (at most once per 64 pages)
+                x.cb = page;
+                x.bidvec = brow[min(page + lane, x.cnt - 1)];
+                // wait here, so that the path without a move carries no wait
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+            const int bid = readlane(x.bidvec, page - x.cb);
+            const int64_t off = (int64_t)bid * a.blk + gk + (int64_t)(gs - page * a.bs) * a.tok;
+            const uint16_t *kb = a.k + off;
+            const uint16_t *vb = a.v + off;
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kb + (col * tok32 + kd[c]));
+            // uniform row pointer per step, one lane offset for all steps
+#pragma unroll
+            for (int i = 0; i < NS; ++i) ld_v<VE>(vb + (int64_t)(VR * i) * a.tok + vlane, r.v[i]);
+        } else {
+            const int last = min(gs + 15, x.t1 - 1);
+            if (page_of((uint32_t)last, a.bs_magic) - x.cb >= 64) {
+                x.cb = page_of((uint32_t)gs, a.bs_magic);
+                x.bidvec = brow[min(x.cb + lane, x.cnt - 1)];
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+            // tokens past t1 read the group's first token instead (in bounds)
+            const int tk = gs + col < x.t1 ? gs + col : gs;
+            const int pk = page_of((uint32_t)tk, a.bs_magic);
+            const int bk = __shfl(x.bidvec, pk - x.cb, 64);
+            const uint16_t *kp = a.k + ((int64_t)bk * a.blk + gk + (int64_t)(tk - pk * a.bs) * a.tok);
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kp + kd[c]);
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const int tv = gs + VR * i + vr < x.t1 ? gs + VR * i + vr : gs;
+                const int pv = page_of((uint32_t)tv, a.bs_magic);
+                const int bv = VR == 1 ? readlane(x.bidvec, pv - x.cb) : __shfl(x.bidvec, pv - x.cb, 64);
+                const uint16_t *vp = a.v + ((int64_t)bv * a.blk + gk + (int64_t)(tv - pv * a.bs) * a.tok);
+                ld_v<VE>(vp + vofs, r.v[i]);
+            }
+        }
+    };
+
+    float m2[GC];          // running max per head (base 2, wave-uniform)
+    float ls4[4];          // running sum of this lane's token weights, head 4 (lane / 16) + i
+    float acc_o[GC][VE];   // running P.V of the lane's elements (partial over its V rows when VR > 1)
+
+    auto compute = [&](const Item<DP> &x, GroupRegs<DP> &r, int n) {
+        const int gs = x.t0 + 16 * n;
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NCK; ++c)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.q[c]),
+                                                           __builtin_bit_cast(bf16x8, r.k[c]), sacc, 0, 0, 0);
+        const bool valid = gs + col < x.t1;
+        float sc[4], rm[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) rm[i] = row_max16(sc[i]);
+        bool grow = false;
+        float alpha[GC];
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+            const float mn = fmaxf(m2[h], readlanef(rm[h & 3], 16 * (h >> 2)));
+            grow |= mn > m2[h];
+            alpha[h] = exp2_fast(m2[h] - mn);   // 0 while m2 is still -inf
+            m2[h] = mn;
+        }
+        if (grow) {   // wave-uniform
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc_o[h][e] *= alpha[h];
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) ls4[i] *= (HR > 1 && row == 1) ? alpha[(4 + i) % GC] : alpha[i];
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float mh = (HR > 1 && row == 1) ? m2[(4 + i) % GC] : m2[i];
+            p[i] = valid ? exp2_fast(sc[i] - mh) : 0.f;
+            ls4[i] += p[i];
+        }
+        if (row < HR) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                if (4 * row + i < GC) ws.p[col][4 * row + i] = p[i];
+        }
+        // the last group may hold rows past t1: zero their V so that
+        // 0 * (NaN or Inf) never reaches the sums
+        if (gs + 16 > x.t1) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const bool ok = gs + VR * i + vr < x.t1;
+#pragma unroll
+                for (int e = 0; e < VE / 2; ++e) r.v[i][e] = ok ? r.v[i][e] : 0u;
+            }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            float pv[GC];
+#pragma unroll
+            for (int h = 0; h < GC; ++h) pv[h] = ws.p[VR * i + vr][h];
+#pragma unroll
+            for (int e = 0; e < VE / 2; ++e) {
+                const float f0 = bf_lo(r.v[i][e]);
+                const float f1 = bf_hi(r.v[i][e]);
 #pragma unroll
                 for (int h = 0; h < GC; ++h) {
-                    if (h >= nh) continue;
-                    const int64_t r = row0 + h;
-                    if (TILE) {
-                        const float ls = a.l[r], ms = a.m[r] * kLog2e;
-                        float Mt = m2[h], fs = 0.f, fp = 1.f;
-                        if (ls > 0.f) {
-                            Mt = fmaxf(ms, m2[h]);
-                            fs = exp2_fast(ms - Mt);
-                            fp = exp2_fast(m2[h] - Mt);
-                        }
-                        if (store) {
-#pragma unroll
-                            for (int e = 0; e < VPL; ++e) {
-                                if (e0 + e >= a.D) continue;
-                                float *po = a.o + r * a.D + e0 + e;
-                                *po = fmaf(*po, fs, acc_o[h][e] * fp);
-                            }
-                        }
-                        if (lane == 0) {
-                            const float Lt = fmaf(ls, fs, lsum[h] * fp);
-                            a.l[r] = Lt;
-                            a.m[r] = Lt > 0.f ? Mt * kLn2 : -INFINITY;
-                        }
-                    } else if (store) {
-                        const float L = lsum[h];
-#pragma unroll
-                        for (int e = 0; e < VPL; ++e)
-                            if (e0 + e < a.D) a.out[r * a.D + e0 + e] = L > 0.f ? f32_to_bf16(acc_o[h][e] / L) : 0;
-                    }
+                    acc_o[h][2 * e] = fmaf(pv[h], f0, acc_o[h][2 * e]);
+                    acc_o[h][2 * e + 1] = fmaf(pv[h], f1, acc_o[h][2 * e + 1]);
                 }
-            } else {
-                // a split partial for the combine kernel
+            }
+        }
+        wave_lds_sync();
+    };
+
+    // The item's totals: its result directly, or a partial.
+    auto finish = [&](const Item<DP> &x) {
+        const int64_t row0 = (int64_t)x.s * a.Hq + x.h0;
+        float rs[4], lsum[GC];
 #pragma unroll
-                for (int h = 0; h < GC; ++h) {
-                    if (h >= nh) continue;
-                    const int64_t pi = (row0 + h) * a.nsplit + slot;
+        for (int i = 0; i < NI; ++i) rs[i] = row_sum16(ls4[i]);
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+            lsum[h] = readlanef(rs[h & 3], 16 * (h >> 2));
+            if constexpr (VR > 1) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc_o[h][e] += shfl_xor(acc_o[h][e], 32);
+            }
+        }
+        // lanes of V row 0 hold the item's totals for elements ve0 .. ve0 + VE - 1
+        const bool store = vr == 0 && vok;
+        if (x.nsp == 1) {
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+                if (h >= x.nh) continue;
+                const int64_t r = row0 + h;
+                if (TILE) {
+                    const float ls = a.l[r], ms = a.m[r] * kLog2e;
+                    float Mt = m2[h], fs = 0.f, fp = 1.f;
+                    if (ls > 0.f) {
+                        Mt = fmaxf(ms, m2[h]);
+                        fs = exp2_fast(ms - Mt);
+                        fp = exp2_fast(m2[h] - Mt);
+                    }
                     if (store) {
+                        float *po = a.o + r * a.D + ve0;
+                        float t[VE];
+                        ld_f<VE>(po, t);
 #pragma unroll
-                        for (int e = 0; e < VPL; ++e)
-                            if (e0 + e < a.D) a.part_o[pi * a.D + e0 + e] = acc_o[h][e];
+                        for (int e = 0; e < VE; ++e) t[e] = fmaf(t[e], fs, acc_o[h][e] * fp);
+                        st_f<VE>(po, t);
                     }
                     if (lane == 0) {
-                        a.part_ml[2 * pi] = m2[h];
-                        a.part_ml[2 * pi + 1] = lsum[h];
+                        const float Lt = fmaf(ls, fs, lsum[h] * fp);
+                        a.l[r] = Lt;
+                        a.m[r] = Lt > 0.f ? Mt * kLn2 : -INFINITY;
                     }
+                } else if (store) {
+                    const float L = lsum[h];
+                    uint32_t packed[VE / 2];
+#pragma unroll
+                    for (int e = 0; e < VE / 2; ++e)
+                        packed[e] = L > 0.f ? (uint32_t)f32_to_bf16(acc_o[h][2 * e] / L) |
+                                                  ((uint32_t)f32_to_bf16(acc_o[h][2 * e + 1] / L) << 16)
+                                            : 0u;
+                    st_u<VE / 2>(a.out + r * a.D + ve0, packed);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+                if (h >= x.nh) continue;
+                const int64_t pi = (row0 + h) * a.nsplit + x.slot;
+                if (store) st_f<VE>(a.part_o + pi * a.D + ve0, acc_o[h]);
+                if (lane == 0) {
+                    a.part_ml[2 * pi] = m2[h];
+                    a.part_ml[2 * pi + 1] = lsum[h];
                 }
             }
         }
-        const int grabbed = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
-        it = nwaves + readlane(grabbed, 0);
+    };
+
+    Item<DP> cur, nxt;
+    GroupRegs<DP> rb[NBUF];
+    take_sync((int)blockIdx.x * kWaves + w, cur);
+    if (cur.kind == 0) {
+#pragma unroll
+        for (int j = 0; j < NBUF - 1; ++j) issue(cur, j, rb[j]);
+    }
+    while (cur.kind == 0) {
+        // The item's q rows and page-id window were requested a round before
+        // the previous item ended.  Consume them here, once per item, so that
+        // no wait for them is left inside the ring loop.
+        asm volatile("" ::"v"(cur.bidvec));
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) asm volatile("" ::"v"(cur.q[c]));
+#pragma unroll
+        for (int h = 0; h < GC; ++h) {
+            m2[h] = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc_o[h][e] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ls4[i] = 0.f;
+
+        // rounds of NBUF groups; the item's group count is padded to whole
+        // rounds (padding re-reads the last group and is not computed)
+        const int nr = (cur.ng + NBUF - 1) / NBUF;
+        const bool staged = nr >= 3;
+        const int rA = staged ? nr - 3 : -1, rB = staged ? nr - 2 : -1;
+        int grabbed = 0, it_next = nitems, cnt_raw = 0, lv_raw = 0;
+        nxt.kind = 2;
+        if (!staged) {
+            // a short item takes the next one at once, waiting at each step
+            it_next = claim_next();
+            locate(it_next, nxt);
+            fetch(nxt, cnt_raw, lv_raw);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            resolve(nxt, cnt_raw, lv_raw);
+        }
+        int n = 0;
+        for (int r = 0; r < nr - 1; ++r, n += NBUF) {
+            // Stage B (locate the claimed item, request its counts, q rows and
+            // page ids) sits before stage A (the claim) in program order, so
+            // every path from the claim to its use, and from the requests to
+            // theirs, crosses a full round of ring loads and the compiler's
+            // waits leave the ring in flight.
+            if (r == rB) {
+                it_next = nwaves + readlane(grabbed, 0);
+                locate(it_next, nxt);
+                fetch(nxt, cnt_raw, lv_raw);
+            }
+            if (r == rA) grabbed = lane == 0 ? atomicAdd(&a.ctrl[0], 1) : 0;
+#pragma unroll
+            for (int j = 0; j < NBUF; ++j) {
+                issue(cur, n + j + NBUF - 1, rb[(j + NBUF - 1) % NBUF]);
+                if (n + j < cur.ng) compute(cur, rb[j], n + j);
+            }
+        }
+        if (staged) resolve(nxt, cnt_raw, lv_raw);   // stage C
+        // last round: its issues after the first carry the next item's first
+        // groups into the ring slots that item starts from
+        issue(cur, n + NBUF - 1, rb[NBUF - 1]);
+        if (n < cur.ng) compute(cur, rb[0], n);
+#pragma unroll
+        for (int j = 1; j < NBUF; ++j) {
+            // both paths issue the same loads, so that the waits of the
+            // computes that follow keep their in-flight allowance
+            if (nxt.kind == 0) issue(nxt, j - 1, rb[j - 1]);
+            else issue(cur, cur.ng - 1, rb[j - 1]);
+            if (n + j < cur.ng) compute(cur, rb[j], n + j);
+        }
+        finish(cur);
+        if (nxt.kind != 0 && it_next < nitems) {
+            // the claimed item had no tokens: take items synchronously
+            if (nxt.kind == 1) {
+                const int64_t row0 = (int64_t)nxt.s * a.Hq + nxt.h0;
+                for (int idx = lane; idx < nxt.nh * a.D; idx += 64) a.out[row0 * a.D + idx] = 0;
+            }
+            take_sync(claim_next(), nxt);
+            if (nxt.kind == 0) {
+#pragma unroll
+                for (int j = 0; j < NBUF - 1; ++j) issue(nxt, j, rb[j]);
+            }
+        }
+        cur = nxt;
     }
 
     // The last wave to finish rewinds the work counter for the next launch.
