@@ -106,15 +106,17 @@ int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
 
 /* Device workspace bytes for max_seqs sequences with the given
  * blocks_per_split (0 = the library's choice, sized for any device): 256 bytes
- * of control words (a work counter) followed by the fp32 split partials,
- * max_seqs * num_q_heads * slots * (head_dim + 2) * 4, where slots is the
- * most partial slots one sequence can need: at most ceil(tile_capacity / bps)
- * (fewer when max_seqs <= 16384, since the kernel then groups most splits
- * four at a time).
+ * of control words (work counters, then the work-item sizing one launch
+ * passes from its attention kernel to its merge kernel) followed by the fp32
+ * split partials, max_seqs * num_q_heads * slots * (head_dim + 2) * 4, where
+ * slots is the most partial slots one sequence can need: at most
+ * ceil(tile_capacity / bps) (fewer when max_seqs <= 16384, since the kernel
+ * then groups most of a sequence's splits into larger work items).
  * The workspace must be zero-filled before its first use; every call that
- * completes leaves the control words zero again, so a workspace is reused
- * without clearing.  Calls that share a workspace must not run concurrently
- * (order them on one stream).  0 if dims are invalid. */
+ * completes leaves the work counters (the first two control words) zero
+ * again, so a workspace is reused without clearing.  Calls that share a
+ * workspace must not run concurrently (order them on one stream).  0 if dims
+ * are invalid. */
 size_t pda_workspace_bytes(const pda_dims *dims, int32_t blocks_per_split);
 
 /* ([TA] paged_strides) layout [num_blocks, block_size, num_kv_heads, head_dim]:

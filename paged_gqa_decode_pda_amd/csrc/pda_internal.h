@@ -8,12 +8,15 @@
 namespace pda {
 
 // Layout of the caller's workspace, in this order:
-//   ctrl      64 int32: [0] next work item, [1] finished waves
+//   ctrl      64 int32: [0] next work item, [1] finished waves; [32..33]
+//             (the next 128-byte line) item sizing passed from the attention
+//             kernel to the merge kernel
 //   part_ml   fp32 [max_seqs, Hq, nsplit, 2]: (m in log2 units, l) per split
 //   part_o    fp32 [max_seqs, Hq, nsplit, D]
-// ctrl must be zero before a launch; every launch that completes leaves it
-// zero again.
+// ctrl[0..1] must be zero before a launch; every launch that completes leaves
+// them zero again.
 constexpr int kCtrlInts = 64;
+constexpr int kCtrlSizing = 32;
 
 // Everything the attention kernel needs, passed by value.
 struct AttendArgs {
@@ -47,6 +50,18 @@ Plan choose_plan(int G, int D, int bs);
 
 // Sequences up to this count enumerate work items through an LDS prefix sum.
 constexpr int kPrefixMaxSeqs = 16384;
+
+// Work-item sizing with the prefix enumeration (decided in the attention
+// kernel from the total work): "big" items span kBigTokensLarge tokens and
+// take kEighthsLarge / 8 of a sequence's splits when there are at least
+// kBigTokensLarge tokens of work per wave, else kBigTokensSmall and
+// kEighthsSmall / 8; a big item is at least one split.  The attention kernel
+// leaves its choice (splits per big item, eighths) in control words
+// kCtrlSizing and kCtrlSizing + 1 for the merge kernel.
+constexpr int kBigTokensSmall = 512;
+constexpr int kBigTokensLarge = 1024;
+constexpr int kEighthsSmall = 6;
+constexpr int kEighthsLarge = 7;
 
 // Launches the persistent attention kernel and, when sequences may have
 // several splits, the combine kernel (decode when a.out is set, else a tile

@@ -45,7 +45,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = 4;
-constexpr int kBigSplits = 4;   // splits per big work item
 constexpr int kThreads = 64 * kWaves;
 
 // The two bf16 halves of a dword, widened exactly to fp32.
@@ -65,11 +64,16 @@ __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x,
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// The work counter is rewound with an agent-scope store (gfx950: sc1, written
-// through to the device coherence point) so that the next launch, on any XCD,
-// sees it.
+// Control words shared across XCDs (the work counter, rewound for the next
+// launch; the item sizing, passed to the merge kernel) are written with
+// agent-scope stores (gfx950: sc1, written through to the device coherence
+// point) and the sizing is read back with agent-scope vector loads.
 __device__ __forceinline__ void st_coherent_i(int *p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The matching vector load from the coherence point (never the scalar cache).
+__device__ __forceinline__ int ld_coherent_i(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0): this wave's vector memory operations completed
 
@@ -216,13 +220,12 @@ struct WaveSmem {
 __device__ __forceinline__ int splits_of(int ntok, int span) { return ntok > 0 ? (ntok + span - 1) / span : 0; }
 
 // Work items of a sequence with nsp splits (prefix mode): nb "big" items of
-// kBigSplits consecutive splits cover about 3/4 of the splits, then one item
-// per remaining split.  Items are numbered in token order; item k of the
-// sequence owns partial slot k, so a sequence has nb + (nsp - nb * kBigSplits)
-// slots.
-__device__ __forceinline__ int big_items_of(int nsp) { return (3 * nsp) / (4 * kBigSplits); }
-__device__ __forceinline__ int slots_of(int nsp, bool prefix_mode) {
-    return prefix_mode ? nsp - (kBigSplits - 1) * big_items_of(nsp) : nsp;
+// `big` consecutive splits cover about eighths / 8 of the splits, then one
+// item per remaining split.  Items are numbered in token order; item k of the
+// sequence owns partial slot k, so a sequence has nb + (nsp - nb * big) slots.
+__device__ __forceinline__ int big_items_of(int nsp, int big, int eighths) { return (eighths * nsp) / (8 * big); }
+__device__ __forceinline__ int slots_of(int nsp, bool prefix_mode, int big, int eighths) {
+    return prefix_mode ? nsp - (big - 1) * big_items_of(nsp, big, eighths) : nsp;
 }
 
 // One work item as a wave holds it.  Everything is wave-uniform except bidvec
@@ -236,6 +239,11 @@ struct Item {
     int bidvec;      // the window: lane i holds the id of page cb + i
     u32x4 q[DP / 32];  // MFMA A operand: head lane % 16, elements 32 c + 8 (lane / 16) .. + 8
 };
+
+// Waves per SIMD the attention kernel is compiled for: two where the
+// registers fit without spilling (head dim up to 64, or 128 with up to four
+// q heads per item), else one.
+constexpr int waves_per_simd(int dp, int gc) { return (dp <= 64 || (dp == 128 && gc <= 4)) ? 2 : 1; }
 
 // Persistent attention kernel.  Work items are (sequence, split, unit), unit =
 // (kv head, head chunk) fastest, so the waves reading the interleaved kv-head
@@ -260,7 +268,8 @@ struct Item {
 // decode, folded into the running state for a tile); otherwise every item
 // leaves an (m, l, o) partial in its slot for combine_kernel.
 template <int DP, int GC, bool P16, int NBUF, bool TILE>
-__global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd(DP, GC))))
+attend_kernel(const AttendArgs a) {
     constexpr int NCK = DP / 32;
     constexpr int VE = VLayout<DP>::VE, VL = VLayout<DP>::VL, VR = VLayout<DP>::VR, NS = VLayout<DP>::NS;
     constexpr int HR = (GC + 3) / 4;   // score rows (of 16 lanes) that hold real heads
@@ -269,6 +278,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 
     __shared__ WaveSmem<GC> wsm[kWaves];
     __shared__ int scan[2 * kWaves];
+    __shared__ float wsum_f[kWaves];
     extern __shared__ int prefix[];   // 2 (S + 1) ints when a.prefix_mode
 
     const int tid = threadIdx.x;
@@ -279,7 +289,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     const int row = lane >> 4, col = lane & 15;
 
     // Work items.  With the prefix (sequences up to kPrefixMaxSeqs), each
-    // sequence's splits are grouped: about 3/4 of them, kBigSplits at a time,
+    // sequence's splits are grouped: a share of them, `big` at a time,
     // form "big" items queued first; the rest are single-split items queued
     // after all big ones, so the queue ends with short work.  Decode keeps
     // one small item for an empty sequence so that its zero output row gets
@@ -288,15 +298,37 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     int *pbig = prefix;                 // big items before sequence s
     int *psmall = prefix + a.S + 1;     // small items before sequence s
     const int nsp_max = (a.cap + a.bps - 1) / a.bps;
+    int big = 1, eighths = 0;
     if (a.prefix_mode) {
+        // Sizing: with at least kBigTokensLarge tokens of work per wave, big
+        // items span kBigTokensLarge tokens and take kEighthsLarge / 8 of the
+        // splits; with less, kBigTokensSmall and kEighthsSmall / 8.  Every
+        // workgroup takes the same decision from the same totals.
+        float tot = 0.f;
+        for (int s = tid; s < a.S; s += kThreads) {
+            const int nt = seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs);
+            psmall[s + 1] = nt;   // kept for the scan below
+            tot += (float)nt;
+        }
+        tot = wave_sum(tot);
+        if (lane == 0) wsum_f[w] = tot;
+        __syncthreads();
+        tot = wsum_f[0] + wsum_f[1] + wsum_f[2] + wsum_f[3];
+        const bool large = tot * (float)units >= (float)kBigTokensLarge * (float)((int)gridDim.x * kWaves);
+        big = max(1, (large ? kBigTokensLarge : kBigTokensSmall) / span);
+        eighths = large ? kEighthsLarge : kEighthsSmall;
+        if (blockIdx.x == 0 && tid == 0) {   // for the merge kernel
+            st_coherent_i(&a.ctrl[kCtrlSizing], big);
+            st_coherent_i(&a.ctrl[kCtrlSizing + 1], eighths);
+        }
         int carry_b = 0, carry_s = 0;
         for (int base = 0; base < a.S; base += kThreads) {
             const int s = base + tid;
             int nb = 0, ns = 0;
             if (s < a.S) {
-                const int nsp = splits_of(seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs), span);
-                nb = big_items_of(nsp);
-                ns = nsp - nb * kBigSplits;
+                const int nsp = splits_of(psmall[s + 1], span);
+                nb = big_items_of(nsp, big, eighths);
+                ns = nsp - nb * big;
                 if (!TILE && nsp == 0) ns = 1;
             }
             int xb = nb, xs = ns;
@@ -369,9 +401,9 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
         int pair = it / units;
         const int unit = it - pair * units;
         if (a.prefix_mode) {
-            const bool big = pair < nbig_pairs;
-            const int *pf = big ? pbig : psmall;
-            if (!big) pair -= nbig_pairs;
+            const bool is_big = pair < nbig_pairs;
+            const int *pf = is_big ? pbig : psmall;
+            if (!is_big) pair -= nbig_pairs;
             int lo = 0, hi = a.S;   // the largest s with pf[s] <= pair
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
@@ -380,13 +412,13 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
             }
             x.s = __builtin_amdgcn_readfirstlane(lo);
             const int j = pair - __builtin_amdgcn_readfirstlane(pf[x.s]);
-            if (big) {
-                x.split = j * kBigSplits;
-                x.nspl = kBigSplits;
+            if (is_big) {
+                x.split = j * big;
+                x.nspl = big;
                 x.slot = j;
             } else {
                 const int nb_s = __builtin_amdgcn_readfirstlane(pbig[x.s + 1] - pbig[x.s]);
-                x.split = nb_s * kBigSplits + j;
+                x.split = nb_s * big + j;
                 x.nspl = 1;
                 x.slot = nb_s + j;
             }
@@ -754,13 +786,16 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 
 // One wave per (sequence, q head) row whose sequence has more than one split:
 // log-sum-exp merge of the split partials in split order (after the running
-// state when folding a tile), into the bf16 output or the state.  Split
-// weights are formed lane-parallel (lane i <-> split cbase + i); lanes own
-// DP/64 consecutive elements of the weighted sums.
+// state when folding a tile), into the bf16 output or the state.  Slot weights
+// are formed lane-parallel (lane i <-> slot cb + i).  The weighted sum reads
+// 16 bytes per lane: a load instruction covers SPI slot rows of DP/4 lanes
+// each, U instructions are in flight, and the SPI lane groups are summed at
+// the end.
 template <int DP, bool TILE>
 __global__ void __launch_bounds__(kThreads) combine_kernel(const AttendArgs a) {
-    constexpr int EPL = DP / 64;
-    __shared__ float wts[kWaves][64];
+    constexpr int LPS = DP / 4;     // lanes per slot row
+    constexpr int SPI = 64 / LPS;   // slot rows per load instruction: 4, 2, 1
+    constexpr int U = 8;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t sh = (int64_t)blockIdx.x * kWaves + w;
@@ -769,67 +804,95 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(const AttendArgs a) {
     const int span = a.bps * a.bs;
     const int nsp = splits_of(seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs), span);
     if (nsp <= 1) return;   // written by the attention kernel (or an untouched empty tile)
-    const int nslot = slots_of(nsp, a.prefix_mode != 0);
-    const int d0 = lane * EPL;
-    const bool dok = d0 < a.D;   // head_dim is a multiple of 8: a lane's elements are all in or all out
+    const bool pm = a.prefix_mode != 0;
+    const int big = pm ? ld_coherent_i(&a.ctrl[kCtrlSizing]) : 1;
+    const int eighths = pm ? ld_coherent_i(&a.ctrl[kCtrlSizing + 1]) : 0;
+    const int nslot = slots_of(nsp, pm, big, eighths);
+    const int sub = lane / LPS;
+    const int d0 = (lane % LPS) * 4;
+    const bool dok = d0 < a.D;   // head_dim is a multiple of 8: a lane's 4 elements are all in or all out
+    const int dofs = dok ? d0 : 0;
     const float *ml = a.part_ml + sh * a.nsplit * 2;
     const float *po = a.part_o + sh * a.nsplit * a.D;
+
+    // Rows of slots j0 + u SPI + sub (u < U) of a chunk with n slots; slots
+    // past n re-read slot n - 1 and get weight 0.
+    float t[U][4];
+    auto load_block = [&](int cb, int j0, int n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = min(j0 + u * SPI + sub, n - 1);
+            ld_f<4>(po + (int64_t)(cb + j) * a.D + dofs, t[u]);
+        }
+    };
+    // (m, l) of slot lane + 64 c
+    auto load_ml = [&](int cb) {
+        float x[2];
+        ld_f<2>(ml + 2 * min(cb + lane, nslot - 1), x);
+        return f32x2{x[0], cb + lane < nslot ? x[1] : 0.f};
+    };
+    // the first chunk's (m, l) and first block of rows do not depend on the
+    // weights: request them before the maximum is known
+    f32x2 ml_c = load_ml(0);
+    load_block(0, 0, min(64, nslot));
 
     const float ls = TILE ? a.l[sh] : 0.f;
     const float ms = TILE ? a.m[sh] * kLog2e : -INFINITY;
     float M = ls > 0.f ? ms : -INFINITY;
-    for (int i = lane; i < nslot; i += 64) {
-        const float li = ml[2 * i + 1], mi = ml[2 * i];
-        if (li > 0.f) M = fmaxf(M, mi);
+    if (ml_c[1] > 0.f) M = fmaxf(M, ml_c[0]);
+    for (int cb = 64; cb < nslot; cb += 64) {
+        const f32x2 x = load_ml(cb);
+        if (x[1] > 0.f) M = fmaxf(M, x[0]);
     }
     M = wave_max(M);
 
-    float L = 0.f, O[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) O[e] = 0.f;
+    float L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
     if (ls > 0.f) {
         const float f = exp2_fast(ms - M);
         L = ls * f;
-        if (dok) {
+        if (sub == 0 && dok) {   // counted once: lane group 0 only
+            float st[4];
+            ld_f<4>(a.o + sh * a.D + d0, st);
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) O[e] = a.o[sh * a.D + d0 + e] * f;
+            for (int e = 0; e < 4; ++e) O[e] = st[e] * f;
         }
     }
     for (int cb = 0; cb < nslot; cb += 64) {
-        const int i = cb + lane;
-        float wi = 0.f, li = 0.f;
-        if (i < nslot) {
-            li = ml[2 * i + 1];
-            const float mi = ml[2 * i];
-            wi = li > 0.f ? exp2_fast(mi - M) : 0.f;
-        }
-        wts[w][lane] = wi;
-        L += wave_sum(wi * li);
-        wave_lds_sync();
+        if (cb > 0) ml_c = load_ml(cb);
+        const float wi = ml_c[1] > 0.f ? exp2_fast(ml_c[0] - M) : 0.f;
+        L += wave_sum(wi * ml_c[1]);
         const int n = min(64, nslot - cb);
-        if (dok) {
-#pragma unroll 8
-            for (int j = 0; j < n; ++j) {
-                const float f = wts[w][j];
-                const float *src = po + (int64_t)(cb + j) * a.D + d0;
+        for (int j0 = 0; j0 < n; j0 += SPI * U) {
+            if (cb > 0 || j0 > 0) load_block(cb, j0, n);
 #pragma unroll
-                for (int e = 0; e < EPL; ++e) O[e] = fmaf(src[e], f, O[e]);
+            for (int u = 0; u < U; ++u) {
+                const int j = j0 + u * SPI + sub;
+                const float f = __shfl(wi, min(j, n - 1), 64);
+                const float fw = j < n ? f : 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[e] = fmaf(t[u][e], fw, O[e]);
             }
         }
-        wave_lds_sync();
     }
-    if (TILE) {
-        if (dok) {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) a.o[sh * a.D + d0 + e] = O[e];
-        }
+    for (int off = LPS; off < 64; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] += shfl_xor(O[e], off);
+    }
+    if (sub != 0 || !dok) return;
+    if (TILE) {
+        st_f<4>(a.o + sh * a.D + d0, O);
         if (lane == 0) {
             a.l[sh] = L;
             a.m[sh] = L > 0.f ? M * kLn2 : -INFINITY;
         }
-    } else if (dok) {
+    } else {
+        uint32_t packed[2];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) a.out[sh * a.D + d0 + e] = L > 0.f ? f32_to_bf16(O[e] / L) : 0;
+        for (int e = 0; e < 2; ++e)
+            packed[e] = L > 0.f ? (uint32_t)f32_to_bf16(O[2 * e] / L) | ((uint32_t)f32_to_bf16(O[2 * e + 1] / L) << 16)
+                                : 0u;
+        st_u<2>(a.out + sh * a.D + d0, packed);
     }
 }
 

@@ -281,8 +281,8 @@ def test_full_size_configs_sampled(cfg):
 
 def test_workspace_reuse_across_calls():
     """One workspace serves many calls with different data and split counts:
-    the control words and tickets a call leaves behind must be zero and no
-    call may read another call's split partials."""
+    the work counters a call leaves behind must be zero and no call may read
+    another call's split partials."""
     announce("workspace reuse")
     shape = dict(S=4, Hq=8, Hkv=2, D=128, bs=16)
     cases = []
@@ -298,7 +298,8 @@ def test_workspace_reuse_across_calls():
                 out = d.decode(bps=bps, ws=ws)
                 assert_parity(out_to_f64(out), ref, label=f"rep {rep} bps {bps}")
     ints = ws.view(devs[0].torch.int32).cpu().numpy()
-    assert np.all(ints[:64] == 0)                 # control words
+    assert np.all(ints[:32] == 0)                 # work counters (and unused words)
+    assert np.all(ints[34:64] == 0)               # unused control words
 
 
 @pytest.mark.parametrize("D", [8, 40, 64, 96, 128, 136, 200, 248, 256])
