@@ -1,13 +1,19 @@
 """Benchmark: paged GQA decode attention on one MI355X.
 
-One step is one pda_decode call (split-KV partial kernel + log-sum-exp combine
+One step is one pda_decode call (split-KV attention kernel + log-sum-exp merge
 kernel) over the ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
 head_dim 128, block_size 16, contexts log-uniform in [128, 32768], 1 % of keys
-scaled by 4, paged layout.  Inputs are seeded synthetic bf16, resident in HBM
-before the timed region.  Prints one JSON line.
+scaled by 4, paged layout (workload "ragged-b64"; the other named workloads
+run the same way, tiled ones as begin_step + step_tile per tile + finalize).  Inputs
+are seeded synthetic bf16, resident in HBM before the timed region.  Prints
+one JSON line: `value` from the timed steps; `roofline.achieved` from the
+attention kernel's own average duration, taken with an event pair around each
+of its launches in a second pass over the same steps; `roofline.traffic` from
+the committed counter summary when the kernel sources still match it.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-                    [--blocks-per-split N] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--blocks-per-split N] [--no-cpu-baseline] [--no-kernel-events]
+    python bench.py --copy-calibration [--copy-mib M]   (counter calibration copy)
 """
 import argparse
 import json
@@ -27,11 +33,17 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="ragged-b64",
+                    choices=["tiny", "llama3-8b-b16", "ragged-b64", "wide-head-d256", "scratch-b256"])
     ap.add_argument("--blocks-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without the per-launch attention-kernel events")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     return ap.parse_args()
 
 
@@ -58,18 +70,63 @@ def cpu_baseline(w, min_seconds):
                       f"{reps} repetition(s), fp64 C oracle with OpenMP"}
 
 
+def kernel_sources_sha256():
+    """Hash of the HIP sources that decide the attention kernel and its launch."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_gqa_decode_pda_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload_name):
+    """HBM bytes per attention launch from the committed counter summary for
+    this workload, or None when it is missing or the kernel sources changed
+    since the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"attend_kernel_{workload_name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not val or sha.group(1) != kernel_sources_sha256():
+        return None
+    return int(val.group(1))
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of a known size, for scaling the HBM byte
+    counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = args.copy_mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
     import torch
 
     import workloads
     import paged_gqa_decode_pda_amd as pda
 
     log(f"generating workload {args.workload}")
-    w = workloads.config(args.workload)
+    w = workloads.named(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     b, c, v = w.stacked_tiles()
@@ -106,6 +163,34 @@ def main():
                                   S, w.strides, stream)
             pda.pda_finalize(plan, out, S, stream)
 
+    # Per-launch events around the attention kernel (armed before every call
+    # that launches it), created once and recorded once so that they exist.
+    launches = T
+    n_ev = 0 if args.no_kernel_events else args.steps * launches
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in ev_b + ev_a:
+        e.record(stream)
+    arm_iter = [None]
+
+    def arm():
+        if arm_iter[0] is not None:
+            i = next(arm_iter[0])
+            pda.pda_debug_time_attention(ev_b[i], ev_a[i])
+
+    if T == 1:
+        def step_timed():
+            arm()
+            step()
+    else:
+        def step_timed():
+            pda.pda_begin_step(plan, S, stream)
+            for t in range(T):
+                arm()
+                pda.pda_step_tile(plan, q, kp, vp, tables[t], counts[t], lastv[t], w.block_size,
+                                  S, w.strides, stream)
+            pda.pda_finalize(plan, out, S, stream)
+
     log("warmup")
     for _ in range(args.warmup):
         step()
@@ -121,11 +206,32 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
     ms = wall * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    if n_ev:
+        # the same steps again, with every attention launch bracketed by its
+        # own event pair (recording them costs a few microseconds per step,
+        # so they stay out of the region above)
+        log(f"timing {args.steps} steps with per-launch attention-kernel events")
+        arm_iter[0] = iter(range(n_ev))
+        for _ in range(args.steps):
+            step_timed()
+        torch.cuda.synchronize()
+        arm_iter[0] = None
     nbytes = w.algorithmic_bytes()
     tbs = nbytes / (ms * 1e-3) / 1e12
-    achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    kernel_us = None
+    if n_ev:
+        kernel_us = sum(b.elapsed_time(a) for b, a in zip(ev_b, ev_a)) * 1e3 / n_ev
+    # the step's algorithmic bytes, spread evenly over its attention launches
+    bytes_per_launch = nbytes / launches
+    if kernel_us:
+        achieved_gbs = bytes_per_launch / (kernel_us * 1e-6) / 1e9
+        kernel_desc = "attend_kernel (paged split-KV attention), average over the timed launches"
+    else:
+        achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
+        kernel_desc = f"{api} step (all launches)"
+    traffic = committed_traffic(w.name) if kernel_us else None
     res = {
         "metric": "paged decode attention achieved HBM TB/s (K+V+q+out bytes per call / time)",
         "value": round(tbs, 4),
@@ -147,9 +253,12 @@ def main():
                    "algorithmic_bytes": nbytes, "layout": w.layout, "api": api,
                    "blocks_per_split": pda.pda_blocks_per_split(dims, bps),
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": f"{api} step (all launches)",
+        "roofline": {"bound": "hbm", "kernel": kernel_desc,
                      "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                     "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
+                     "launches_per_step": launches},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")

@@ -185,6 +185,15 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
                       int32_t num_seqs, pda_strides strides, void *workspace,
                       size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream);
 
+/* Timing diagnostics, for benchmarks that need the attention kernel's own
+ * duration: arms the calling thread's next pda_decode or pda_step_tile call
+ * to record `before` and `after` (hipEvent_t handles owned by the caller,
+ * passed as void*) on that call's stream right before and right after its
+ * attention kernel, ahead of the split merge.  The next call that launches
+ * the attention kernel consumes the pair; NULL, NULL disarms.  PDA_ERR_NULL
+ * if exactly one of them is NULL. */
+pda_status pda_debug_time_attention(void *before, void *after);
+
 /* Static name of a status code. */
 const char *pda_status_string(pda_status status);
 

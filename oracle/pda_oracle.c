@@ -26,7 +26,7 @@
  *  - same page, TiledAttentionDims::validate and gqa_ratio: q heads are a
  *    whole multiple of kv heads, their ratio G being passed to the kernel.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - q head h reads kv head g = h / G (contiguous groups of G q heads).
  *  - the last-valid count is given per sequence and per tile; it applies to the
  *    last page that tile lists for the sequence, every other page being full.

@@ -41,7 +41,8 @@ for _i, _n in enumerate(STATUS_NAMES):
 EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_blocks_per_split",
             "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
             "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
-            "pda_step_tile", "pda_finalize", "pda_decode", "pda_status_string", "pda_last_error"]
+            "pda_step_tile", "pda_finalize", "pda_decode", "pda_debug_time_attention",
+            "pda_status_string", "pda_last_error"]
 
 
 class pda_dims(ctypes.Structure):
@@ -91,6 +92,7 @@ _sig("pda_step_tile", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_
 _sig("pda_finalize", ctypes.c_int, _P, _P, _i32, _P)
 _sig("pda_decode", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P, _sz,
      _P, _i32, _P)
+_sig("pda_debug_time_attention", ctypes.c_int, _P, _P)
 _sig("pda_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("pda_last_error", ctypes.c_char_p)
 
@@ -219,6 +221,18 @@ def pda_step_tile(plan, q, k_pool, v_pool, tile_blocks, tile_block_counts, last_
 
 def pda_finalize(plan, out, num_seqs: int, stream=None) -> None:
     _check(_lib.pda_finalize(plan, _addr(out), num_seqs, _stream(stream)))
+
+
+def pda_debug_time_attention(before, after) -> None:
+    """Arms the next attention launch on this thread to record two events
+    around its attention kernel.  Events are torch.cuda.Event objects that
+    have been recorded once (so that they exist), raw hipEvent_t integers, or
+    None, None to disarm."""
+    def handle(e):
+        if e is None or isinstance(e, int):
+            return e
+        return e.cuda_event
+    _check(_lib.pda_debug_time_attention(handle(before), handle(after)))
 
 
 def pda_decode(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,

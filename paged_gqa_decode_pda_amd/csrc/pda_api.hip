@@ -80,6 +80,15 @@ int device_cus() {
 // [8, 64] pages (never below ceil(tile_capacity / 256)): long page lists get
 // longer splits, so that a sequence's split count, and with it the combine
 // work, stays bounded.
+// Events armed by pda_debug_time_attention for this thread's next launch.
+thread_local pda::AttendEvents t_events;
+
+pda::AttendEvents take_events() {
+    const pda::AttendEvents ev = t_events;
+    t_events = pda::AttendEvents{};
+    return ev;
+}
+
 int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
     (void)num_seqs;
     const int32_t cap = d->tile_capacity;
@@ -325,7 +334,7 @@ pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, cons
     a.m = plan->m;
     a.l = plan->l;
     a.o = plan->o;
-    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream));
+    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "tile launch");
 }
 
@@ -373,8 +382,17 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
                                     last_block_valid, last_block_valid_default, strides, bps,
                                     workspace, num_seqs, p);
     a.out = static_cast<uint16_t *>(out);
-    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream));
+    hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "decode launch");
+}
+
+pda_status pda_debug_time_attention(void *before, void *after) {
+    clear_err();
+    if ((before == nullptr) != (after == nullptr))
+        return fail(PDA_ERR_NULL, "both events or neither must be given");
+    t_events.before = static_cast<hipEvent_t>(before);
+    t_events.after = static_cast<hipEvent_t>(after);
+    return PDA_OK;
 }
 
 const char *pda_status_string(pda_status s) {

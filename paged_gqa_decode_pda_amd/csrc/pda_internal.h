@@ -66,7 +66,15 @@ constexpr int kEighthsLarge = 7;
 // Launches the persistent attention kernel and, when sequences may have
 // several splits, the combine kernel (decode when a.out is set, else a tile
 // folded into the running state).  `cus` is the device's compute-unit count.
-hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st);
+// Optional events recorded on the launch stream right before and right after
+// the attention kernel (timing diagnostics); null members are skipped.
+struct AttendEvents {
+    hipEvent_t before = nullptr;
+    hipEvent_t after = nullptr;
+};
+
+hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st,
+                         const AttendEvents &ev);
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st);
 hipError_t launch_finalize(const float *l, const float *o, uint16_t *out, int64_t rows, int D,
                            hipStream_t st);

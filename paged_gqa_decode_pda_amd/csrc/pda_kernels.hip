@@ -32,9 +32,6 @@
 //      Softmax weights move from the score layout to the V layout through LDS.
 #include "pda_internal.h"
 
-#include <map>
-#include <mutex>
-#include <utility>
 
 namespace pda {
 namespace {
@@ -240,11 +237,6 @@ struct Item {
     u32x4 q[DP / 32];  // MFMA A operand: head lane % 16, elements 32 c + 8 (lane / 16) .. + 8
 };
 
-// Waves per SIMD the attention kernel is compiled for: two where the
-// registers fit without spilling (head dim up to 64, or 128 with up to four
-// q heads per item), else one.
-constexpr int waves_per_simd(int dp, int gc) { return (dp <= 64 || (dp == 128 && gc <= 4)) ? 2 : 1; }
-
 // Persistent attention kernel.  Work items are (sequence, split, unit), unit =
 // (kv head, head chunk) fastest, so the waves reading the interleaved kv-head
 // rows of the same pages run together.  Every wave takes items from an atomic
@@ -268,8 +260,7 @@ constexpr int waves_per_simd(int dp, int gc) { return (dp <= 64 || (dp == 128 &&
 // decode, folded into the running state for a tile); otherwise every item
 // leaves an (m, l, o) partial in its slot for combine_kernel.
 template <int DP, int GC, bool P16, int NBUF, bool TILE>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd(DP, GC))))
-attend_kernel(const AttendArgs a) {
+__global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     constexpr int NCK = DP / 32;
     constexpr int VE = VLayout<DP>::VE, VL = VLayout<DP>::VL, VR = VLayout<DP>::VR, NS = VLayout<DP>::NS;
     constexpr int HR = (GC + 3) / 4;   // score rows (of 16 lanes) that hold real heads
@@ -918,34 +909,29 @@ __global__ void __launch_bounds__(256) finalize_kernel(const float *l, const flo
     }
 }
 
-// Workgroups per compute unit the kernel can hold, cached per (kernel, LDS).
-int blocks_per_cu(const void *kernel, size_t dyn_lds) {
-    static std::mutex mu;
-    static std::map<std::pair<const void *, size_t>, int> cache;
-    std::lock_guard<std::mutex> lock(mu);
-    auto key = std::make_pair(kernel, dyn_lds);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kThreads, dyn_lds) != hipSuccess || n < 1) n = 1;
-    cache[key] = n;
-    return n;
-}
-
-constexpr int nbuf_for(int dp) { return dp == 256 ? 2 : 3; }   // 16-token K/V groups in flight per wave
+// Ring slots (16-token K/V groups; all but one in flight per wave): three,
+// two for head dim 256 (measured faster there: 32 KB in flight per wave).
+constexpr int nbuf_for(int dp) { return dp == 256 ? 2 : 3; }
 
 template <int DP, int GC, bool P16, bool TILE>
-hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st) {
+hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
     auto kernel = attend_kernel<DP, GC, P16, nbuf_for(DP), TILE>;
     const size_t dyn = a.prefix_mode ? 2 * sizeof(int) * ((size_t)a.S + 1) : 0;
-    const int64_t per_cu = blocks_per_cu(reinterpret_cast<const void *>(kernel), dyn);
+    // One workgroup (four waves) per compute unit: measured on MI355X, the
+    // paged row streams of one wave per SIMD reach a higher HBM rate than two
+    // (or an uneven split of workgroups over the CUs).
     const int64_t nsp_max = (a.cap + a.bps - 1) / a.bps;
     const int64_t upper = ((int64_t)a.S * nsp_max * a.Hkv * a.nhc + kWaves - 1) / kWaves;
-    int64_t nwg = per_cu * cus;
+    int64_t nwg = cus;
     if (nwg > upper) nwg = upper;
     if (nwg < 1) nwg = 1;
+    if (ev.before) {
+        const hipError_t r = hipEventRecord(ev.before, st);
+        if (r != hipSuccess) return r;
+    }
     hipLaunchKernelGGL(kernel, dim3((unsigned)nwg), dim3(kThreads), dyn, st, a);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && ev.after) e = hipEventRecord(ev.after, st);
     if (e != hipSuccess || a.bps >= a.cap) return e;   // one split per sequence: nothing to combine
     const int64_t rows = (int64_t)a.S * a.Hq;
     hipLaunchKernelGGL((combine_kernel<DP, TILE>), dim3((unsigned)((rows + kWaves - 1) / kWaves)),
@@ -954,20 +940,23 @@ hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st) {
 }
 
 template <int DP, int GC>
-hipError_t launch_attend_p(const Plan &p, const AttendArgs &a, int cus, hipStream_t st) {
+hipError_t launch_attend_p(const Plan &p, const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
     const bool tile = a.out == nullptr;
-    if (p.p16) return tile ? launch_attend_t<DP, GC, true, true>(a, cus, st) : launch_attend_t<DP, GC, true, false>(a, cus, st);
-    return tile ? launch_attend_t<DP, GC, false, true>(a, cus, st) : launch_attend_t<DP, GC, false, false>(a, cus, st);
+    if (p.p16)
+        return tile ? launch_attend_t<DP, GC, true, true>(a, cus, st, ev)
+                    : launch_attend_t<DP, GC, true, false>(a, cus, st, ev);
+    return tile ? launch_attend_t<DP, GC, false, true>(a, cus, st, ev)
+                : launch_attend_t<DP, GC, false, false>(a, cus, st, ev);
 }
 
 template <int DP>
-hipError_t launch_attend_g(const Plan &p, const AttendArgs &a, int cus, hipStream_t st) {
+hipError_t launch_attend_g(const Plan &p, const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
     switch (p.gc) {
-        case 1: return launch_attend_p<DP, 1>(p, a, cus, st);
-        case 2: return launch_attend_p<DP, 2>(p, a, cus, st);
-        case 4: return launch_attend_p<DP, 4>(p, a, cus, st);
+        case 1: return launch_attend_p<DP, 1>(p, a, cus, st, ev);
+        case 2: return launch_attend_p<DP, 2>(p, a, cus, st, ev);
+        case 4: return launch_attend_p<DP, 4>(p, a, cus, st, ev);
         default:
-            if constexpr (DP <= 128) return launch_attend_p<DP, 8>(p, a, cus, st);
+            if constexpr (DP <= 128) return launch_attend_p<DP, 8>(p, a, cus, st, ev);
             return hipErrorInvalidValue;
     }
 }
@@ -992,11 +981,12 @@ Plan choose_plan(int G, int D, int bs) {
     return p;
 }
 
-hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st) {
+hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st,
+                         const AttendEvents &ev) {
     switch (p.dp) {
-        case 64: return launch_attend_g<64>(p, a, cus, st);
-        case 128: return launch_attend_g<128>(p, a, cus, st);
-        default: return launch_attend_g<256>(p, a, cus, st);
+        case 64: return launch_attend_g<64>(p, a, cus, st, ev);
+        case 128: return launch_attend_g<128>(p, a, cus, st, ev);
+        default: return launch_attend_g<256>(p, a, cus, st, ev);
     }
 }
 

@@ -28,21 +28,21 @@ def oracle_of(dev: Device, tiles=None):
     return oracle.attend(p.q, p.pool, p.k_base, p.v_base, p.strides, p.Hkv, p.bs, b, c, v)
 
 
-def test_config1_decode_and_tiled():
-    announce("cfg1 decode + tiled")
-    w = workloads.config(1)
+def test_tiny_workload_decode_and_tiled():
+    announce("tiny workload decode + tiled")
+    w = workloads.named("tiny")
     dev = Device(w)
     ref = oracle.attend_workload(w)
     got = out_to_f64(dev.decode())
-    e = assert_parity(got, ref["out"], label="cfg1 decode")
+    e = assert_parity(got, ref["out"], label="tiny decode")
     state, out = dev.tiled()
-    assert_parity(out_to_f64(out), ref["out"], label="cfg1 tiled")
+    assert_parity(out_to_f64(out), ref["out"], label="tiny tiled")
     m, l, o = dev.split_state(state)
     # state: natural-log max, and l, o relative to it
     np.testing.assert_allclose(m, ref["m"], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(l * np.exp(m - ref["m"]), ref["l"], rtol=1e-4)
     np.testing.assert_allclose(o / l[..., None], ref["out"], rtol=0, atol=1e-4)
-    print("cfg1 max/mean err", e)
+    print("tiny max/mean err", e)
 
 
 SMALL = [
@@ -257,16 +257,16 @@ def test_last_valid_scalar_default():
     np.testing.assert_array_equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
-def test_full_size_configs_sampled(cfg):
+@pytest.mark.parametrize("name", ["llama3-8b-b16", "ragged-b64", "wide-head-d256", "scratch-b256"])
+def test_full_size_workloads_sampled(name):
     """The named workloads at full size, in the launch configuration the
     benchmark times (automatic split size), checked on a sample of (sequence,
     q head) pairs evaluated one by one by the oracle."""
-    announce("full config", cfg)
-    w = workloads.config(cfg)
+    announce("full-size workload", name)
+    w = workloads.named(name)
     dev = Device(w)
     S, Hq = w.num_seqs, w.num_q_heads
-    rng = np.random.default_rng(cfg)
+    rng = np.random.default_rng(workloads.WORKLOADS[name][0])
     pairs = np.unique(np.concatenate([rng.choice(S * Hq, size=min(S * Hq, 96), replace=False),
                                       [0, S * Hq - 1]]))
     ref = oracle.attend_workload(w, pairs=pairs)
@@ -275,8 +275,8 @@ def test_full_size_configs_sampled(cfg):
     else:
         _, out = dev.tiled()
     got = out_to_f64(out).reshape(S * Hq, w.head_dim)[pairs]
-    e = assert_parity(got, ref["out"], label=f"cfg{cfg}")
-    print(f"cfg{cfg} sampled max/mean err {e}")
+    e = assert_parity(got, ref["out"], label=name)
+    print(f"{name} sampled max/mean err {e}")
 
 
 def test_workspace_reuse_across_calls():

@@ -219,3 +219,15 @@ def test_small_blocks_per_split_accepted_on_host():
         pda.pda_decode(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, st, FAKE, FAKE, 1, stream=0,
                        workspace_bytes=16)
     assert e.value.status == pda.PDA_ERR_WORKSPACE
+
+
+def test_debug_time_attention_arming():
+    """The timing hook takes both events or neither; arming and disarming
+    touch no device."""
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_debug_time_attention(FAKE, None)
+    assert e.value.status == pda.PDA_ERR_NULL
+    with pytest.raises(pda.PdaError):
+        pda.pda_debug_time_attention(None, FAKE)
+    pda.pda_debug_time_attention(FAKE, FAKE + 64)
+    pda.pda_debug_time_attention(None, None)

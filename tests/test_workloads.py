@@ -56,8 +56,8 @@ def test_layout_strides_match_numpy_shapes():
     assert workloads.layout_strides("scratch", Hkv, D, bs) == (st[0], st[3], st[2])
 
 
-def test_config1_structure():
-    w = workloads.config(1)
+def test_tiny_structure():
+    w = workloads.named("tiny")
     assert (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size) == (1, 4, 1, 64, 16)
     assert w.contexts.tolist() == [100]
     t = w.tiles[0]
@@ -110,7 +110,7 @@ def test_peaked_keys_scaled_by_four():
 
 
 @pytest.mark.slow
-def test_config_sizes():
-    w = workloads.config(2)
+def test_llama3_b16_sizes():
+    w = workloads.named("llama3-8b-b16")
     assert w.num_seqs == 16 and 512 <= w.contexts.min() and w.contexts.max() <= 4096
     assert w.strides == (16384, 1024, 128)

@@ -327,41 +327,42 @@ def make_workload(*, name: str, seed: int, num_seqs: int, num_q_heads: int, num_
                     tile_capacity=cap, seed=seed)
 
 
-CONFIG_NAMES = {
-    1: "tiny: S=1 Hq/Hkv=4/1 D=64 bs=16 ctx=100 paged, one tile",
-    2: "llama3-8b-b16: S=16 Hq/Hkv=32/8 D=128 bs=16 ctx~U[512,4096] paged",
-    3: "ragged-b64: S=64 Hq/Hkv=32/8 D=128 bs=16 ctx~logU[128,32768] paged, 1% keys x4",
-    4: "wide-head: S=4 Hq/Hkv=16/8 D=256 bs=16 ctx=65536 paged, 8 tiles of 512 pages",
-    5: "scratch-b256: S=256 Hq/Hkv=32/8 D=128 bs=16 ctx~U[2048,8192] scratch, 4 tiles",
+# The named workloads: name -> (seed, description).
+WORKLOADS = {
+    "tiny": (1001, "S=1 Hq/Hkv=4/1 D=64 bs=16 ctx=100 paged, one tile"),
+    "llama3-8b-b16": (1002, "S=16 Hq/Hkv=32/8 D=128 bs=16 ctx~U[512,4096] paged"),
+    "ragged-b64": (1003, "S=64 Hq/Hkv=32/8 D=128 bs=16 ctx~logU[128,32768] paged, 1% keys x4"),
+    "wide-head-d256": (1004, "S=4 Hq/Hkv=16/8 D=256 bs=16 ctx=65536 paged, 8 tiles of 512 pages"),
+    "scratch-b256": (1005, "S=256 Hq/Hkv=32/8 D=128 bs=16 ctx~U[2048,8192] scratch, 4 tiles"),
 }
 
 
-def config(n: int) -> Workload:
-    """The five named workloads; seed = 1000 + n."""
-    seed = 1000 + n
+def named(name: str) -> Workload:
+    """One of the named workloads (see WORKLOADS), built from its fixed seed."""
+    if name not in WORKLOADS:
+        raise ValueError(f"unknown workload {name!r}; one of {sorted(WORKLOADS)}")
+    seed = WORKLOADS[name][0]
     rng = np.random.Generator(np.random.PCG64(seed))
-    if n == 1:
-        return make_workload(name="cfg1-tiny", seed=seed, num_seqs=1, num_q_heads=4,
+    if name == "tiny":
+        return make_workload(name=name, seed=seed, num_seqs=1, num_q_heads=4,
                              num_kv_heads=1, head_dim=64, block_size=16, contexts=[100],
                              placement="choice", pool_pages=32, tile_capacity=8, rng=rng)
-    if n == 2:
+    if name == "llama3-8b-b16":
         ctx = rng.integers(512, 4096, endpoint=True, size=16)
-        return make_workload(name="cfg2-llama3-8b-b16", seed=seed, num_seqs=16, num_q_heads=32,
+        return make_workload(name=name, seed=seed, num_seqs=16, num_q_heads=32,
                              num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
                              tile_capacity=256, rng=rng)
-    if n == 3:
+    if name == "ragged-b64":
         u = rng.uniform(np.log(128.0), np.log(32768.0), size=64)
         ctx = np.clip(np.floor(np.exp(u)).astype(np.int64), 128, 32768)
-        return make_workload(name="cfg3-ragged-b64", seed=seed, num_seqs=64, num_q_heads=32,
+        return make_workload(name=name, seed=seed, num_seqs=64, num_q_heads=32,
                              num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
                              tile_capacity=2048, rng=rng, peak_fraction=0.01, peak_scale=4.0)
-    if n == 4:
-        return make_workload(name="cfg4-wide-head", seed=seed, num_seqs=4, num_q_heads=16,
+    if name == "wide-head-d256":
+        return make_workload(name=name, seed=seed, num_seqs=4, num_q_heads=16,
                              num_kv_heads=8, head_dim=256, block_size=16,
                              contexts=[65536] * 4, n_tiles=8, tile_capacity=512, rng=rng)
-    if n == 5:
-        ctx = rng.integers(2048, 8192, endpoint=True, size=256)
-        return make_workload(name="cfg5-scratch-b256", seed=seed, num_seqs=256, num_q_heads=32,
-                             num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
-                             layout="scratch", n_tiles=4, tile_capacity=128, rng=rng)
-    raise ValueError(n)
+    ctx = rng.integers(2048, 8192, endpoint=True, size=256)
+    return make_workload(name=name, seed=seed, num_seqs=256, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
+                         layout="scratch", n_tiles=4, tile_capacity=128, rng=rng)
