@@ -109,9 +109,8 @@ int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
  * of control words (work counters, then the work-item sizing one launch
  * passes from its attention kernel to its merge kernel) followed by the fp32
  * split partials, max_seqs * num_q_heads * slots * (head_dim + 2) * 4, where
- * slots is the most partial slots one sequence can need: at most
- * ceil(tile_capacity / bps) (fewer when max_seqs <= 16384, since the kernel
- * then groups most of a sequence's splits into larger work items).
+ * slots = ceil(tile_capacity / bps), one per split (the kernel may group
+ * splits into larger work items, which then share a slot).
  * The workspace must be zero-filled before its first use; every call that
  * completes leaves the work counters (the first two control words) zero
  * again, so a workspace is reused without clearing.  Calls that share a

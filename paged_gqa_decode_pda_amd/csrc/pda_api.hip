@@ -105,25 +105,12 @@ int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
 // sequences the kernel groups about 3/4 of a sequence's splits four at a
 // time, so a sequence with n splits has n - 3 * floor(3n / 16) slots;
 // beyond that every split has its own slot.
-// Partial slots one (sequence, q head) row can need: with the prefix
-// enumeration a sequence of n splits has n - (big - 1) * floor(e n / (8 big))
-// items, each with its own slot, for either sizing the attention kernel may
-// choose (big items of at least one split); without it, one slot per split.
+// Partial slots one (sequence, q head) row can need: one per item.  A
+// sequence of n splits has n items when every split is an item, and
+// n - (big - 1) * floor(e n / (8 big)) with big items (never more), so n
+// bounds both sizings the attention kernel may choose.
 int64_t slots_per_seq(const pda_dims *d, int32_t bps) {
-    const int64_t nsp = ceil_div(d->tile_capacity, bps);
-    if (d->max_seqs > pda::kPrefixMaxSeqs) return nsp;
-    const int64_t span = (int64_t)bps * d->block_size;
-    const int64_t sizing[2][2] = {{pda::kBigTokensSmall, pda::kEighthsSmall},
-                                  {pda::kBigTokensLarge, pda::kEighthsLarge}};
-    int64_t best = 1;
-    for (const auto &z : sizing) {
-        const int64_t big = z[0] / span < 1 ? 1 : z[0] / span;
-        for (int64_t n = 1; n <= nsp; ++n) {
-            const int64_t slots = n - (big - 1) * ((z[1] * n) / (8 * big));
-            if (slots > best) best = slots;
-        }
-    }
-    return best;
+    return ceil_div(d->tile_capacity, bps);
 }
 
 int64_t units_of(const pda_dims *d) {

@@ -52,16 +52,16 @@ Plan choose_plan(int G, int D, int bs);
 constexpr int kPrefixMaxSeqs = 16384;
 
 // Work-item sizing with the prefix enumeration (decided in the attention
-// kernel from the total work): "big" items span kBigTokensLarge tokens and
-// take kEighthsLarge / 8 of a sequence's splits when there are at least
-// kBigTokensLarge tokens of work per wave, else kBigTokensSmall and
-// kEighthsSmall / 8; a big item is at least one split.  The attention kernel
-// leaves its choice (splits per big item, eighths) in control words
-// kCtrlSizing and kCtrlSizing + 1 for the merge kernel.
-constexpr int kBigTokensSmall = 512;
+// kernel from the total work): with at least kBigTokensLarge tokens of work
+// per wave, "big" items span kBigTokensLarge tokens (at least one split) and
+// take kEighthsLarge / 8 of a sequence's splits; with less, every split is an
+// item of its own when that makes no more items than waves, else
+// kEighthsPaired / 8 of the splits go in pairs.  The attention kernel leaves
+// its choice (splits per big item, eighths) in control words kCtrlSizing and
+// kCtrlSizing + 1 for the merge kernel.
 constexpr int kBigTokensLarge = 1024;
-constexpr int kEighthsSmall = 6;
 constexpr int kEighthsLarge = 7;
+constexpr int kEighthsPaired = 6;
 
 // Launches the persistent attention kernel and, when sequences may have
 // several splits, the combine kernel (decode when a.out is set, else a tile

@@ -269,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 
     __shared__ WaveSmem<GC> wsm[kWaves];
     __shared__ int scan[2 * kWaves];
-    __shared__ float wsum_f[kWaves];
+    __shared__ float wsum_f[2 * kWaves];
     extern __shared__ int prefix[];   // 2 (S + 1) ints when a.prefix_mode
 
     const int tid = threadIdx.x;
@@ -291,23 +291,39 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     const int nsp_max = (a.cap + a.bps - 1) / a.bps;
     int big = 1, eighths = 0;
     if (a.prefix_mode) {
-        // Sizing: with at least kBigTokensLarge tokens of work per wave, big
+        // Sizing (every workgroup takes the same decision from the same
+        // totals): with at least kBigTokensLarge tokens of work per wave, big
         // items span kBigTokensLarge tokens and take kEighthsLarge / 8 of the
-        // splits; with less, kBigTokensSmall and kEighthsSmall / 8.  Every
-        // workgroup takes the same decision from the same totals.
-        float tot = 0.f;
+        // splits; with less, every split is an item as long as there are no
+        // more split items than waves (one round, equal lengths), else
+        // kEighthsPaired / 8 of the splits go in pairs.
+        float tot = 0.f, nspl = 0.f;
         for (int s = tid; s < a.S; s += kThreads) {
             const int nt = seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs);
             psmall[s + 1] = nt;   // kept for the scan below
             tot += (float)nt;
+            nspl += (float)splits_of(nt, span);
         }
         tot = wave_sum(tot);
-        if (lane == 0) wsum_f[w] = tot;
+        nspl = wave_sum(nspl);
+        if (lane == 0) {
+            wsum_f[w] = tot;
+            wsum_f[kWaves + w] = nspl;
+        }
         __syncthreads();
         tot = wsum_f[0] + wsum_f[1] + wsum_f[2] + wsum_f[3];
-        const bool large = tot * (float)units >= (float)kBigTokensLarge * (float)((int)gridDim.x * kWaves);
-        big = max(1, (large ? kBigTokensLarge : kBigTokensSmall) / span);
-        eighths = large ? kEighthsLarge : kEighthsSmall;
+        nspl = wsum_f[4] + wsum_f[5] + wsum_f[6] + wsum_f[7];
+        const float waves = (float)((int)gridDim.x * kWaves);
+        if (tot * (float)units >= (float)kBigTokensLarge * waves) {
+            big = max(1, kBigTokensLarge / span);
+            eighths = kEighthsLarge;
+        } else if (nspl * (float)units > waves) {
+            big = 2;
+            eighths = kEighthsPaired;
+        } else {
+            big = 1;
+            eighths = 0;
+        }
         if (blockIdx.x == 0 && tid == 0) {   // for the merge kernel
             st_coherent_i(&a.ctrl[kCtrlSizing], big);
             st_coherent_i(&a.ctrl[kCtrlSizing + 1], eighths);

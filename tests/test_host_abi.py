@@ -102,15 +102,9 @@ def test_state_and_workspace_sizes():
     for bps in (1, 3, 32, 100):
         eff = min(bps, 32)
         assert pda.pda_blocks_per_split(d, bps) == eff
-        # 64 control ints, then the partials: the most slots a sequence of up
-        # to ceil(32 / bps) splits needs when 6/8 of its splits go into big
-        # items of 512 tokens, or 7/8 into items of 1024 tokens (a big item
-        # is at least one split), and the rest one by one
-        nsp = -(-32 // eff)
-        slots = max(n - (big - 1) * ((e * n) // (8 * big))
-                    for tokens, e in ((512, 6), (1024, 7))
-                    for big in [max(1, tokens // (eff * 16))]
-                    for n in range(1, nsp + 1))
+        # 64 control ints, then the partials: one slot per split of a
+        # sequence of up to ceil(32 / bps) splits
+        slots = -(-32 // eff)
         assert pda.pda_workspace_bytes(d, bps) == 64 * 4 + rows * slots * (64 + 2) * 4
     auto = pda.pda_blocks_per_split(d, 0)
     assert 1 <= auto <= 32
