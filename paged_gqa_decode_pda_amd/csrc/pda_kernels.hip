@@ -210,7 +210,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // to the V layout (16 lanes per token row).
 template <int GC>
 struct WaveSmem {
-    float p[16][GC];
+    float p[2][16][GC];   // double-buffered by group parity
 };
 
 // Splits of a sequence: ceil(ntok / span), 0 for an empty sequence.
@@ -555,7 +555,15 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     float ls4[4];          // running sum of this lane's token weights, head 4 (lane / 16) + i
     float acc_o[GC][VE];   // running P.V of the lane's elements (partial over its V rows when VR > 1)
 
-    auto compute = [&](const Item<DP> &x, GroupRegs<DP> &r, int n) {
+    // Per group, two stages, software-pipelined across groups: scores(g + 1)
+    // (MFMA, online max, weights into LDS buffer (g + 1) & 1) runs next to
+    // pv(g) (weights of group g from buffer g & 1, times V), so the latency
+    // chain of one overlaps the FMAs of the other.  The rescale of the P.V
+    // sums by the max change of group g + 1 is applied after pv(g).
+    bool grow_next = false;   // wave-uniform
+    float alpha_next[GC];
+
+    auto scores = [&](const Item<DP> &x, GroupRegs<DP> &r, int n) {
         const int gs = x.t0 + 16 * n;
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -569,22 +577,17 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) rm[i] = row_max16(sc[i]);
         bool grow = false;
-        float alpha[GC];
 #pragma unroll
         for (int h = 0; h < GC; ++h) {
             const float mn = fmaxf(m2[h], readlanef(rm[h & 3], 16 * (h >> 2)));
             grow |= mn > m2[h];
-            alpha[h] = exp2_fast(m2[h] - mn);   // 0 while m2 is still -inf
+            alpha_next[h] = exp2_fast(m2[h] - mn);   // 0 while m2 is still -inf
             m2[h] = mn;
         }
-        if (grow) {   // wave-uniform
+        grow_next = grow;
+        if (grow) {
 #pragma unroll
-            for (int h = 0; h < GC; ++h) {
-#pragma unroll
-                for (int e = 0; e < VE; ++e) acc_o[h][e] *= alpha[h];
-            }
-#pragma unroll
-            for (int i = 0; i < NI; ++i) ls4[i] *= (HR > 1 && row == 1) ? alpha[(4 + i) % GC] : alpha[i];
+            for (int i = 0; i < NI; ++i) ls4[i] *= (HR > 1 && row == 1) ? alpha_next[(4 + i) % GC] : alpha_next[i];
         }
         float p[4];
 #pragma unroll
@@ -596,8 +599,12 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
         if (row < HR) {
 #pragma unroll
             for (int i = 0; i < NI; ++i)
-                if (4 * row + i < GC) ws.p[col][4 * row + i] = p[i];
+                if (4 * row + i < GC) ws.p[n & 1][col][4 * row + i] = p[i];
         }
+    };
+
+    auto pv = [&](const Item<DP> &x, GroupRegs<DP> &r, int n) {
+        const int gs = x.t0 + 16 * n;
         // the last group may hold rows past t1: zero their V so that
         // 0 * (NaN or Inf) never reaches the sums
         if (gs + 16 > x.t1) {
@@ -608,21 +615,51 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
                 for (int e = 0; e < VE / 2; ++e) r.v[i][e] = ok ? r.v[i][e] : 0u;
             }
         }
-        wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            float pv[GC];
+            float pw[GC];
 #pragma unroll
-            for (int h = 0; h < GC; ++h) pv[h] = ws.p[VR * i + vr][h];
+            for (int h = 0; h < GC; ++h) pw[h] = ws.p[n & 1][VR * i + vr][h];
 #pragma unroll
             for (int e = 0; e < VE / 2; ++e) {
                 const float f0 = bf_lo(r.v[i][e]);
                 const float f1 = bf_hi(r.v[i][e]);
 #pragma unroll
                 for (int h = 0; h < GC; ++h) {
-                    acc_o[h][2 * e] = fmaf(pv[h], f0, acc_o[h][2 * e]);
-                    acc_o[h][2 * e + 1] = fmaf(pv[h], f1, acc_o[h][2 * e + 1]);
+                    acc_o[h][2 * e] = fmaf(pw[h], f0, acc_o[h][2 * e]);
+                    acc_o[h][2 * e + 1] = fmaf(pw[h], f1, acc_o[h][2 * e + 1]);
                 }
+            }
+        }
+    };
+
+    // Group g of the current item: scores(g + 1) from ring slot NEXT, pv(g)
+    // from ring slot THIS, then the rescale for group g + 1.  With a ring of
+    // two slots the next group is the one just requested, so there the
+    // stages stay in group order (scores(g), then pv(g)).
+    constexpr bool kPipelined = NBUF >= 3;
+    auto step = [&](const Item<DP> &x, GroupRegs<DP> &rthis, GroupRegs<DP> &rnext, int g) {
+        grow_next = false;
+        if constexpr (kPipelined) {
+            if (g + 1 < x.ng) scores(x, rnext, g + 1);
+        } else {
+            scores(x, rthis, g);
+            if (grow_next) {
+#pragma unroll
+                for (int h = 0; h < GC; ++h) {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) acc_o[h][e] *= alpha_next[h];
+                }
+            }
+            grow_next = false;
+            wave_lds_sync();
+        }
+        pv(x, rthis, g);
+        if (grow_next) {
+#pragma unroll
+            for (int h = 0; h < GC; ++h) {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) acc_o[h][e] *= alpha_next[h];
             }
         }
         wave_lds_sync();
@@ -733,6 +770,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             resolve(nxt, cnt_raw, lv_raw);
         }
+        if constexpr (kPipelined) {
+            scores(cur, rb[0], 0);   // the pipeline's first stage for group 0
+            wave_lds_sync();
+        }
         int n = 0;
         for (int r = 0; r < nr - 1; ++r, n += NBUF) {
             // Stage B (locate the claimed item, request its counts, q rows and
@@ -749,21 +790,21 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 #pragma unroll
             for (int j = 0; j < NBUF; ++j) {
                 issue(cur, n + j + NBUF - 1, rb[(j + NBUF - 1) % NBUF]);
-                if (n + j < cur.ng) compute(cur, rb[j], n + j);
+                if (n + j < cur.ng) step(cur, rb[j], rb[(j + 1) % NBUF], n + j);
             }
         }
         if (staged) resolve(nxt, cnt_raw, lv_raw);   // stage C
         // last round: its issues after the first carry the next item's first
         // groups into the ring slots that item starts from
         issue(cur, n + NBUF - 1, rb[NBUF - 1]);
-        if (n < cur.ng) compute(cur, rb[0], n);
+        if (n < cur.ng) step(cur, rb[0], rb[1], n);
 #pragma unroll
         for (int j = 1; j < NBUF; ++j) {
             // both paths issue the same loads, so that the waits of the
             // computes that follow keep their in-flight allowance
             if (nxt.kind == 0) issue(nxt, j - 1, rb[j - 1]);
             else issue(cur, cur.ng - 1, rb[j - 1]);
-            if (n + j < cur.ng) compute(cur, rb[j], n + j);
+            if (n + j < cur.ng) step(cur, rb[j], rb[(j + 1) % NBUF], n + j);
         }
         finish(cur);
         if (nxt.kind != 0 && it_next < nitems) {
@@ -925,9 +966,9 @@ __global__ void __launch_bounds__(256) finalize_kernel(const float *l, const flo
     }
 }
 
-// Ring slots (16-token K/V groups; all but one in flight per wave): three,
-// two for head dim 256 (measured faster there: 32 KB in flight per wave).
-constexpr int nbuf_for(int dp) { return dp == 256 ? 2 : 3; }
+// Ring slots (16-token K/V groups; all but one in flight per wave): four,
+// two for head dim 256 (measured faster there: 16 KB per group).
+constexpr int nbuf_for(int dp) { return dp == 256 ? 2 : 4; }
 
 template <int DP, int GC, bool P16, bool TILE>
 hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
