@@ -94,13 +94,19 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
 
-// VE / 2 dwords of bf16 pairs (VE = 2 or 4 elements).
+
+
+// VE / 2 dwords of bf16 pairs (VE = 2 or 4 elements) of a V row.  V rows
+// are streamed once per call and each load covers whole cache lines, so they
+// are read non-temporally (measured on MI355X: 5-7 % faster steps).  K rows
+// are not: each 128-byte line of a K row is read by two load instructions
+// (64 bytes of 16 rows each), and the second must still find the line.
 template <int VE>
 __device__ __forceinline__ void ld_v(const uint16_t *p, uint32_t (&r)[VE / 2]) {
     if constexpr (VE == 2) {
-        r[0] = *reinterpret_cast<const uint32_t *>(p);
+        r[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
     } else {
-        const u32x2 x = ld8(p);
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
         r[0] = x[0];
         r[1] = x[1];
     }
