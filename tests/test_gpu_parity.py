@@ -279,6 +279,25 @@ def test_full_size_workloads_sampled(name):
     print(f"{name} sampled max/mean err {e}")
 
 
+@pytest.mark.parametrize("S", [16384, 16385])
+def test_many_sequences_both_enumerations(S):
+    """Up to 16384 sequences the kernel enumerates work items through a
+    per-workgroup prefix in LDS (the largest one it holds); one more switches
+    to the plain (sequence, split) enumeration with empty items skipped.
+    Both, on tiny ragged sequences (empty ones included), decode and tiled,
+    with several splits per sequence."""
+    announce("many sequences", S)
+    rng = np.random.Generator(np.random.PCG64(70 + S % 7))
+    ctx = rng.integers(0, 21, size=S)
+    case = build_case(rng, S, 2, 1, 8, 4, ctx, n_tiles=1)
+    dev = Device(case)
+    ref = oracle_of(dev)["out"]
+    for bps in (1, 2):
+        assert_parity(out_to_f64(dev.decode(bps=bps)), ref, label=f"S={S} decode bps={bps}")
+        _, out = dev.tiled(bps=bps)
+        assert_parity(out_to_f64(out), ref, label=f"S={S} tiled bps={bps}")
+
+
 def test_workspace_reuse_across_calls():
     """One workspace serves many calls with different data and split counts:
     the work counters a call leaves behind must be zero and no call may read
