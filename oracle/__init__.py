@@ -48,7 +48,8 @@ def load_library(path):
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.pda_oracle_attend.argtypes = [i32, i32, i32, i32, i32, P, P, i64, i64, i64, i64, i64,
-                                      i64, i32, i32, P, P, P, P, i64, P, P, P, P, ctypes.c_int]
+                                      i64, i32, i32, P, P, P, P, i64, P, i64, P, P, P, P,
+                                      ctypes.c_int]
     lib.pda_oracle_attend.restype = ctypes.c_int
     return lib
 
@@ -76,7 +77,7 @@ def bf16_to_f64(bits) -> np.ndarray:
 
 
 def attend(q, pool, k_base, v_base, strides, num_kv_heads, block_size, blocks, counts,
-           last_valid, pairs=None, threads=None, lib=None):
+           last_valid, pairs=None, threads=None, lib=None, mask=None):
     """Attention of each (sequence, q head) over the tokens its tiles list.
 
     q           uint16 [S, Hq, D] bf16 bits
@@ -85,6 +86,9 @@ def attend(q, pool, k_base, v_base, strides, num_kv_heads, block_size, blocks, c
     blocks      int32 [T, S, capacity] (or [S, capacity] for one tile)
     counts      int32 [T, S] (or [S]);  last_valid likewise
     pairs       optional int array of s*Hq + h to evaluate (default: all)
+    mask        optional bool/uint8 [S, kv_len]: position t of sequence s (logical
+                order over the tiles) is kept where mask[s, t] is true; positions
+                past kv_len must not be listed
     lib         optional ctypes handle of another build of pda_oracle.c (the
                 mutation tests load deliberately broken copies through it)
 
@@ -115,10 +119,16 @@ def attend(q, pool, k_base, v_base, strides, num_kv_heads, block_size, blocks, c
     o = np.empty((n, D), np.float64)
     out = np.empty((n, D), np.float64)
     blk, tok, kvh = (int(x) for x in strides)
+    if mask is not None:
+        mask = np.ascontiguousarray(np.asarray(mask).astype(np.uint8))
+        assert mask.ndim == 2 and mask.shape[0] == S
+        total = _listed_tokens(counts, last_valid, cap, int(block_size))
+        assert np.all(total <= mask.shape[1]), "the mask must cover every listed position"
     rc = (lib or _load()).pda_oracle_attend(
         S, Hq, int(num_kv_heads), D, int(block_size), q.ctypes.data, pool.ctypes.data,
         pool.size, int(k_base), int(v_base), blk, tok, kvh, T, cap, blocks.ctypes.data,
         counts.ctypes.data, last_valid.ctypes.data,
+        None if mask is None else mask.ctypes.data, 0 if mask is None else mask.shape[1],
         None if pairs_arr is None else pairs_arr.ctypes.data, n, m.ctypes.data, l.ctypes.data,
         o.ctypes.data, out.ctypes.data, int(threads or host_threads()))
     if rc != 0:
@@ -127,6 +137,13 @@ def attend(q, pool, k_base, v_base, strides, num_kv_heads, block_size, blocks, c
         return {"m": m.reshape(S, Hq), "l": l.reshape(S, Hq), "o": o.reshape(S, Hq, D),
                 "out": out.reshape(S, Hq, D)}
     return {"m": m, "l": l, "o": o, "out": out}
+
+
+def _listed_tokens(counts, last_valid, cap, block_size):
+    """Tokens each sequence lists over the tiles (counts and last-valid clamped)."""
+    c = np.clip(counts, 0, cap).astype(np.int64)
+    lv = np.clip(last_valid, 0, block_size).astype(np.int64)
+    return np.where(c > 0, (c - 1) * block_size + lv, 0).sum(axis=0)
 
 
 def attend_workload(w, tiles=None, pairs=None, threads=None):

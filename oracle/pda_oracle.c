@@ -25,6 +25,9 @@
  *    and for V alike.
  *  - same page, TiledAttentionDims::validate and gqa_ratio: q heads are a
  *    whole multiple of kv heads, their ratio G being passed to the kernel.
+ *  - AstrAI "CUDA Kernels" page, section "Python Wrappers": an optional
+ *    boolean mask over the kv positions of each sequence, True keeping the
+ *    position ([batch, kv_len] for a single query).
  *
  * Readings where the pages are silent:
  *  - q head h reads kv head g = h / G (contiguous groups of G q heads).
@@ -34,6 +37,9 @@
  *    [0, block_size].
  *  - a sequence with no token gives M = -inf, L = 0, O = 0 and out = 0.
  *  - the state's m is in natural-log units (the max of the scaled scores).
+ *  - the mask indexes a sequence's tokens in logical order (over all tiles
+ *    given); a position it does not keep is left out of the softmax entirely,
+ *    exactly as if the token were not listed.
  *
  * Inputs are bf16 bit patterns; each is widened exactly to binary64 and all
  * arithmetic is binary64.
@@ -57,14 +63,16 @@ static int32_t clamp_i32(int32_t x, int32_t lo, int32_t hi) {
 /*
  * Element offsets (relative to a pool base) of every token row that sequence
  * s lists for kv head g, in logical order: tile by tile, page by page, slot by
- * slot.  Returns the number of rows, or -1 if a row would leave the pool.
+ * slot, leaving out the positions the mask (if any) does not keep.  Returns
+ * the number of rows, or -1 if a row would leave the pool.
  */
 static int64_t gather_rows(int32_t s, int32_t g, int32_t num_seqs, int32_t block_size,
                            int64_t blk, int64_t tok, int64_t kvh, int32_t head_dim,
                            int32_t n_tiles, int32_t capacity, const int32_t *blocks,
                            const int32_t *counts, const int32_t *last_valid,
+                           const uint8_t *mask, int64_t mask_stride,
                            int64_t pool_rows_limit, int64_t *rows) {
-    int64_t n = 0;
+    int64_t n = 0, pos = 0;
     for (int32_t t = 0; t < n_tiles; ++t) {
         int32_t cnt = clamp_i32(counts[(int64_t)t * num_seqs + s], 0, capacity);
         const int32_t *list = blocks + ((int64_t)t * num_seqs + s) * capacity;
@@ -73,6 +81,9 @@ static int64_t gather_rows(int32_t s, int32_t g, int32_t num_seqs, int32_t block
             if (i == cnt - 1)
                 valid = clamp_i32(last_valid[(int64_t)t * num_seqs + s], 0, block_size);
             for (int32_t j = 0; j < valid; ++j) {
+                const int keep = mask == NULL || mask[(int64_t)s * mask_stride + pos] != 0;
+                ++pos;
+                if (!keep) continue;
                 int64_t r = (int64_t)list[i] * blk + (int64_t)j * tok + (int64_t)g * kvh;
                 if (list[i] < 0 || r < 0 || r + head_dim > pool_rows_limit) return -1;
                 rows[n++] = r;
@@ -92,6 +103,9 @@ static int64_t gather_rows(int32_t s, int32_t g, int32_t num_seqs, int32_t block
  *   blocks      int32 [n_tiles, num_seqs, capacity]
  *   counts      int32 [n_tiles, num_seqs]
  *   last_valid  int32 [n_tiles, num_seqs]
+ *   mask        optional uint8 [num_seqs, mask_stride]: position t of sequence
+ *               s (in logical order over the tiles) is kept where
+ *               mask[s * mask_stride + t] != 0 (NULL: every position kept)
  *   pairs       optional list of n_pairs indices s*num_q_heads + h to compute
  *               (NULL: all num_seqs*num_q_heads, in order)
  *   m, l        fp64 [n_pairs]; o, out fp64 [n_pairs, head_dim]
@@ -104,6 +118,7 @@ int pda_oracle_attend(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
                       const uint16_t *pool, int64_t pool_elems, int64_t k_base, int64_t v_base,
                       int64_t blk, int64_t tok, int64_t kvh, int32_t n_tiles, int32_t capacity,
                       const int32_t *blocks, const int32_t *counts, const int32_t *last_valid,
+                      const uint8_t *mask, int64_t mask_stride,
                       const int32_t *pairs, int64_t n_pairs, double *m, double *l, double *o,
                       double *out, int nthreads) {
     if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
@@ -134,7 +149,8 @@ int pda_oracle_attend(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_head
             const int32_t g = h / G;
             double *op = o + p * head_dim, *outp = out + p * head_dim;
             int64_t n = gather_rows(s, g, num_seqs, block_size, blk, tok, kvh, head_dim, n_tiles,
-                                    capacity, blocks, counts, last_valid, row_limit, rows);
+                                    capacity, blocks, counts, last_valid, mask, mask_stride,
+                                    row_limit, rows);
             if (n < 0) {
 #pragma omp atomic write
                 status = -1;

@@ -152,11 +152,13 @@ def build_case(rng: np.random.Generator, S, Hq, Hkv, D, bs, contexts, layout="pa
                 counts, lv, seq_pages, P, ranges)
 
 
-def dense_reference(case: Case, tiles: Optional[int] = None):
+def dense_reference(case: Case, tiles: Optional[int] = None, mask=None):
     """Attention over the dense logical rows with torch's CPU
     scaled_dot_product_attention in float64 (a library routine; the default
     scale of that routine is 1/sqrt(head_dim)).  GQA by repeat_interleave over
-    the head axis, i.e. q head h reads kv head h // G."""
+    the head axis, i.e. q head h reads kv head h // G.  `mask` [S, >= tokens]
+    (True = keep) goes to the routine as its boolean attn_mask; a row that
+    keeps nothing is left 0 here (the routine itself would give NaN)."""
     import torch
     G = case.Hq // case.Hkv
     out = np.zeros((case.S, case.Hq, case.D))
@@ -175,6 +177,12 @@ def dense_reference(case: Case, tiles: Optional[int] = None):
         k = k.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
         v = v.repeat_interleave(G, dim=0).unsqueeze(0).contiguous()
         q = torch.from_numpy(case.qf[s]).unsqueeze(0).unsqueeze(2)  # [1, Hq, 1, D]
-        o = torch.nn.functional.scaled_dot_product_attention(q, k, v)
+        am = None
+        if mask is not None:
+            keep = np.asarray(mask[s][lo:hi], dtype=bool)
+            if not keep.any():
+                continue
+            am = torch.from_numpy(keep).view(1, 1, 1, hi - lo)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am)
         out[s] = o[0, :, 0, :].numpy()
     return out

@@ -258,6 +258,64 @@ def pin_golden_closed_form(attend):
     assert abs(r["l"][0, 0] - L) < 1e-15
 
 
+def _random_mask(rng, contexts, width, p_drop=0.3):
+    m = rng.random((len(contexts), width)) >= p_drop
+    if len(contexts) > 1:
+        m[1, :] = False          # one sequence keeps nothing
+    return m
+
+
+def pin_mask_dense_library(attend):
+    """With a boolean keep-mask over each sequence's positions ([CK] Python
+    Wrappers: mask [batch, kv_len], True = keep) the output equals torch's
+    float64 scaled_dot_product_attention given the same boolean attn_mask
+    (library routine); a sequence that keeps nothing gives 0 and l = 0."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for S, Hq, Hkv, D, bs, ctx, layout, T in DENSE_SHAPES:
+        case = build_case(rng, S, Hq, Hkv, D, bs, ctx, layout=layout, n_tiles=T)
+        mask = _random_mask(rng, ctx, max(ctx) + 3)
+        r = _run(attend, case, mask=mask)
+        np.testing.assert_allclose(r["out"], dense_reference(case, mask=mask), rtol=0,
+                                   atol=1e-12, err_msg=f"{(S, Hq, Hkv, D, bs, ctx, layout, T)}")
+        for s in range(S):
+            if not mask[s, :ctx[s]].any():
+                assert np.all(r["l"][s] == 0.0) and np.all(r["out"][s] == 0.0)
+
+
+def pin_mask_is_removal(attend):
+    """A position the mask drops is as if its token were not listed at all:
+    the masked output equals the unmasked output of a case built from the kept
+    tokens only (same K/V values, other pages)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    S, Hq, Hkv, D, bs = 3, 4, 2, 16, 4
+    ctx = [23, 9, 17]
+    case = build_case(rng, S, Hq, Hkv, D, bs, ctx)
+    mask = rng.random((S, 24)) >= 0.4
+    kept = [np.flatnonzero(mask[s, :ctx[s]]) for s in range(S)]
+
+    def values(s, T):
+        assert T == len(kept[s])
+        return case.K[s][kept[s]], case.V[s][kept[s]]
+
+    small = build_case(np.random.Generator(np.random.PCG64(14)), S, Hq, Hkv, D, bs,
+                       [len(k) for k in kept], values=values, q_values=case.qf)
+    a = _run(attend, case, mask=mask)
+    b = _run(attend, small)
+    np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(a["l"], b["l"], rtol=1e-14, atol=0)
+
+
+def pin_mask_all_keep(attend):
+    """A mask that keeps every position changes nothing, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    case = build_case(rng, S=2, Hq=4, Hkv=1, D=8, bs=5, contexts=[12, 31], n_tiles=2)
+    a = _run(attend, case)
+    b = _run(attend, case, mask=np.ones((2, 40), dtype=bool))
+    for key in ("m", "l", "o", "out"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
 ALL_PINS = [pin_context_one, pin_identical_keys, pin_zero_query, pin_page_permutation,
             pin_dense_library, pin_poison, pin_key_shift, pin_linear_in_v, pin_peaked,
-            pin_golden_closed_form]
+            pin_golden_closed_form, pin_mask_dense_library, pin_mask_is_removal,
+            pin_mask_all_keep]

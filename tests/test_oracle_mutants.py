@@ -24,6 +24,9 @@ MUTANTS = {
                      "for (int32_t d = 1; d < head_dim; ++d) acc +="),
     "no_normalise": ("L > 0.0 ? op[d] / L : 0.0", "L > 0.0 ? op[d] : 0.0"),
     "first_tile_only": ("for (int32_t t = 0; t < n_tiles; ++t)", "for (int32_t t = 0; t < 1; ++t)"),
+    "mask_ignored": ("mask[(int64_t)s * mask_stride + pos] != 0", "1"),
+    "mask_inverted": ("mask[(int64_t)s * mask_stride + pos] != 0", "mask[(int64_t)s * mask_stride + pos] == 0"),
+    "mask_position_per_page": ("                ++pos;\n", ""),
     "q_head_swapped": ("q + ((int64_t)s * num_q_heads + h) * head_dim",
                        "q + ((int64_t)s * num_q_heads + (num_q_heads - 1 - h)) * head_dim"),
 }
