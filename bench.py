@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--mask-drop", type=float, default=None,
+                    help="decode with pda_decode_masked and a seeded random keep-mask dropping "
+                         "this fraction of positions (single-tile workloads)")
     return ap.parse_args()
 
 
@@ -145,7 +148,16 @@ def main():
     stream = torch.cuda.current_stream()
     S = w.num_seqs
 
-    if T == 1:
+    if T == 1 and args.mask_drop is not None:
+        api = f"pda_decode_masked (keep-mask dropping {args.mask_drop:.0%} of positions)"
+        width = int(w.contexts.max()) + 1
+        mrng = np.random.default_rng(7)
+        kv_mask = torch.from_numpy((mrng.random((S, width)) >= args.mask_drop).astype(np.uint8)).to(dev)
+
+        def step():
+            pda.pda_decode_masked(dims, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
+                                  w.strides, kv_mask, width, ws, out, bps, stream)
+    elif T == 1:
         api = "pda_decode"
 
         def step():
@@ -231,7 +243,7 @@ def main():
     else:
         achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
         kernel_desc = f"{api} step (all launches)"
-    traffic = committed_traffic(w.name) if kernel_us else None
+    traffic = committed_traffic(w.name) if kernel_us and args.mask_drop is None else None
     res = {
         "metric": "paged decode attention achieved HBM TB/s (K+V+q+out bytes per call / time)",
         "value": round(tbs, 4),

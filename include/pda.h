@@ -14,9 +14,12 @@
  *        paged_strides, scratch_pool_strides, step_tile, finalize, and the
  *        constant NEG_INF_F32_BITS.
  *  [CK]  AstrAI "CUDA Kernels": section "Python Wrappers" (q/k/v layout
- *        [batch, seq_len, n_heads, head_dim]; scale 1/sqrt(head_dim); wrappers
- *        fail loudly when the compiled library is absent) and the "Overview"
- *        table (GQA decode with split-KV; paged KV-cache decode).
+ *        [batch, seq_len, n_heads, head_dim]; scale 1/sqrt(head_dim); the
+ *        optional boolean mask [batch, kv_len], true keeping a position;
+ *        wrappers fail loudly when the compiled library is absent), section
+ *        "Attention Backend" (decode through the paged kernel with page
+ *        size 1) and the "Overview" table (GQA decode with split-KV; paged
+ *        KV-cache decode).
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
@@ -183,6 +186,25 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
                       const int32_t *last_block_valid, int32_t last_block_valid_default,
                       int32_t num_seqs, pda_strides strides, void *workspace,
                       size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream);
+
+/* pda_decode with a boolean keep-mask over each sequence's kv positions
+ * ([CK] Python Wrappers: mask [batch, kv_len], true = keep).
+ *   kv_mask      device uint8 [num_seqs, mask_stride]: position t of sequence
+ *                s (its t-th listed token, in list order) takes part where
+ *                kv_mask[s * mask_stride + t] != 0
+ *   mask_stride  bytes per sequence row, >= 1 (PDA_ERR_DIMS otherwise)
+ * Other arguments as pda_decode.  A dropped position is left out of the
+ * softmax as if its token were not listed; a sequence whose every position is
+ * dropped gets an all-zero output row.  Device-side contract: each row holds
+ * at least as many bytes as its sequence lists tokens.  PDA_ERR_NULL if
+ * kv_mask is NULL. */
+pda_status pda_decode_masked(const pda_dims *dims, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *block_tables,
+                             const int32_t *block_counts, const int32_t *last_block_valid,
+                             int32_t last_block_valid_default, int32_t num_seqs,
+                             pda_strides strides, const uint8_t *kv_mask, int64_t mask_stride,
+                             void *workspace, size_t workspace_bytes, void *out,
+                             int32_t blocks_per_split, void *stream);
 
 /* Timing diagnostics, for benchmarks that need the attention kernel's own
  * duration: arms the calling thread's next pda_decode or pda_step_tile call

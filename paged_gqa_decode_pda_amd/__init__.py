@@ -41,7 +41,8 @@ for _i, _n in enumerate(STATUS_NAMES):
 EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_blocks_per_split",
             "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
             "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
-            "pda_step_tile", "pda_finalize", "pda_decode", "pda_debug_time_attention",
+            "pda_step_tile", "pda_finalize", "pda_decode", "pda_decode_masked",
+            "pda_debug_time_attention",
             "pda_status_string", "pda_last_error"]
 
 
@@ -92,6 +93,8 @@ _sig("pda_step_tile", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_
 _sig("pda_finalize", ctypes.c_int, _P, _P, _i32, _P)
 _sig("pda_decode", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P, _sz,
      _P, _i32, _P)
+_sig("pda_decode_masked", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P,
+     _i64, _P, _sz, _P, _i32, _P)
 _sig("pda_debug_time_attention", ctypes.c_int, _P, _P)
 _sig("pda_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("pda_last_error", ctypes.c_char_p)
@@ -244,3 +247,70 @@ def pda_decode(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_v
                            _addr(block_tables), _addr(block_counts), _addr(last_block_valid),
                            last_block_valid_default, num_seqs, _strides(strides), _addr(workspace),
                            nb, _addr(out), blocks_per_split, _stream(stream)))
+
+
+def pda_decode_masked(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                      last_block_valid_default: int, num_seqs: int, strides, kv_mask,
+                      mask_stride: int, workspace, out, blocks_per_split: int = 0, stream=None,
+                      workspace_bytes=None) -> None:
+    d = _dims(dims)
+    nb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    _check(_lib.pda_decode_masked(ctypes.byref(d), _addr(q), _addr(k_pool), _addr(v_pool),
+                                  _addr(block_tables), _addr(block_counts),
+                                  _addr(last_block_valid), last_block_valid_default, num_seqs,
+                                  _strides(strides), _addr(kv_mask), int(mask_stride),
+                                  _addr(workspace), nb, _addr(out), blocks_per_split,
+                                  _stream(stream)))
+
+
+def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, mask=None, out=None,
+                      workspace=None, blocks_per_split: int = 0, stream=None):
+    """Decode attention in the calling convention of the pages' paged decode
+    wrapper: q [batch, 1, n_heads, head_dim] bf16 (blhd, one query token),
+    k_cache / v_cache [num_blocks, block_size, n_kv_heads, head_dim] bf16
+    (block_size 1 = token-granular tables), block_table int32 [batch,
+    max_blocks], seq_lens int32 [batch] tokens per sequence, mask optional
+    bool [batch, >= max(seq_lens)] (True = keep).  Scale 1/sqrt(head_dim).
+    Returns out [batch, 1, n_heads, head_dim] bf16.  Everything runs in the
+    library's kernels; this function only derives the C-ABI arguments (page
+    counts and last-page valid slots from seq_lens) and allocates the output
+    and workspace when they are not given."""
+    import torch
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [batch, 1, n_heads, head_dim]")
+    B, _, Hq, D = q.shape
+    nblk, bs, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, n_kv_heads, head_dim]")
+    for t in (q, k_cache, v_cache):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q, k_cache and v_cache must be contiguous bfloat16 tensors")
+        if t.device.type != "cuda":
+            raise ValueError("q, k_cache and v_cache must be device tensors")
+    if block_table.device.type != "cuda":
+        raise ValueError("block_table must be a device tensor")
+    if mask is not None and seq_lens.device.type == "cpu" and seq_lens.numel() and \
+            int(seq_lens.max()) > mask.shape[-1]:
+        raise ValueError("mask rows are shorter than the longest sequence")
+    block_table = block_table.to(torch.int32).contiguous()
+    cap = block_table.shape[1]
+    lens = seq_lens.to(device=block_table.device, dtype=torch.int32)
+    counts = ((lens + (bs - 1)) // bs).to(torch.int32).contiguous()
+    lastv = torch.where(counts > 0, lens - (counts - 1) * bs, torch.zeros_like(lens)).to(torch.int32).contiguous()
+    dims = pda_dims(B, Hq, Hkv, D, bs, cap)
+    strides = pda_paged_strides(dims)
+    if out is None:
+        out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        workspace = torch.zeros(max(1, pda_workspace_bytes(dims, blocks_per_split) // 4),
+                                dtype=torch.float32, device=q.device)
+    if mask is None:
+        pda_decode(dims, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
+                   workspace, out, blocks_per_split, stream)
+    else:
+        m = mask.to(device=q.device, dtype=torch.uint8).contiguous()
+        if m.dim() != 2 or m.shape[0] != B:
+            raise ValueError("mask must be [batch, kv_len]")
+        pda_decode_masked(dims, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
+                          m, m.shape[1], workspace, out, blocks_per_split, stream)
+    return out

@@ -185,6 +185,8 @@ pda::AttendArgs attend_args(const pda_dims *d, const void *q, const void *k, con
     a.part_o = wsf + (int64_t)d->max_seqs * d->num_q_heads * a.nsplit * 2;
     a.out = nullptr;
     a.m = a.l = a.o = nullptr;
+    a.mask = nullptr;
+    a.mask_stride = 0;
     return a;
 }
 
@@ -340,12 +342,14 @@ pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *strea
     return e == hipSuccess ? PDA_OK : hip_fail(e, "finalize launch");
 }
 
-pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
-                      const int32_t *block_tables, const int32_t *block_counts,
-                      const int32_t *last_block_valid, int32_t last_block_valid_default,
-                      int32_t num_seqs, pda_strides strides, void *workspace,
-                      size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream) {
-    clear_err();
+namespace {
+
+pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
+                       const int32_t *block_tables, const int32_t *block_counts,
+                       const int32_t *last_block_valid, int32_t last_block_valid_default,
+                       int32_t num_seqs, pda_strides strides, const uint8_t *kv_mask,
+                       int64_t mask_stride, void *workspace, size_t workspace_bytes, void *out,
+                       int32_t blocks_per_split, void *stream) {
     pda_status st = check_dims(dims);
     if (st != PDA_OK) return st;
     if (num_seqs < 0 || num_seqs > dims->max_seqs)
@@ -369,8 +373,38 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
                                     last_block_valid, last_block_valid_default, strides, bps,
                                     workspace, num_seqs, p);
     a.out = static_cast<uint16_t *>(out);
+    a.mask = kv_mask;
+    a.mask_stride = mask_stride;
     hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "decode launch");
+}
+
+}  // namespace
+
+pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
+                      const int32_t *block_tables, const int32_t *block_counts,
+                      const int32_t *last_block_valid, int32_t last_block_valid_default,
+                      int32_t num_seqs, pda_strides strides, void *workspace,
+                      size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream) {
+    clear_err();
+    return decode_impl(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                       last_block_valid_default, num_seqs, strides, nullptr, 0, workspace,
+                       workspace_bytes, out, blocks_per_split, stream);
+}
+
+pda_status pda_decode_masked(const pda_dims *dims, const void *q, const void *k_pool,
+                             const void *v_pool, const int32_t *block_tables,
+                             const int32_t *block_counts, const int32_t *last_block_valid,
+                             int32_t last_block_valid_default, int32_t num_seqs,
+                             pda_strides strides, const uint8_t *kv_mask, int64_t mask_stride,
+                             void *workspace, size_t workspace_bytes, void *out,
+                             int32_t blocks_per_split, void *stream) {
+    clear_err();
+    if (!kv_mask) return fail(PDA_ERR_NULL, "kv_mask is NULL");
+    if (mask_stride < 1) return fail(PDA_ERR_DIMS, "mask_stride must be >= 1");
+    return decode_impl(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                       last_block_valid_default, num_seqs, strides, kv_mask, mask_stride, workspace,
+                       workspace_bytes, out, blocks_per_split, stream);
 }
 
 pda_status pda_debug_time_attention(void *before, void *after) {

@@ -31,6 +31,8 @@ struct AttendArgs {
     float *part_o;
     uint16_t *out;            // bf16 [S, Hq, D] (decode) or null
     float *m, *l, *o;         // running state (tile) or null
+    const uint8_t *mask;      // decode: kv keep-mask [S, mask_stride] (nonzero = keep) or null
+    int64_t mask_stride;      // bytes per sequence row of the mask
     int64_t blk, tok, kvh;    // strides in bf16 elements
     uint64_t bs_magic;        // ceil(2^32 / bs): t / bs == (t * bs_magic) >> 32 for t < 2^24
     int32_t S, Hq, Hkv, G, D, bs, cap, bps, nhc, nsplit, lv_default;

@@ -171,6 +171,8 @@ template <int DP>
 struct GroupRegs {
     u32x4 k[DP / 32];   // K, MFMA B-operand layout: token lane % 16, elements 32 c + 8 (lane / 16) .. + 8
     uint32_t v[VLayout<DP>::NS][VLayout<DP>::VE / 2];   // V: token VR i + lane / VL, elements VE (lane % VL) .. + VE
+    uint32_t keep;      // with a kv mask: the mask byte of token lane % 16
+    uint64_t kept;      // with a kv mask: bit t set when token t takes part (filled by the scores stage)
 };
 
 __device__ __forceinline__ int readlane(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
@@ -265,7 +267,7 @@ struct Item {
 // sequence with one split gets its result written directly (bf16 o / l for
 // decode, folded into the running state for a tile); otherwise every item
 // leaves an (m, l, o) partial in its slot for combine_kernel.
-template <int DP, int GC, bool P16, int NBUF, bool TILE>
+template <int DP, int GC, bool P16, int NBUF, bool TILE, bool MASK>
 __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
     constexpr int NCK = DP / 32;
     constexpr int VE = VLayout<DP>::VE, VL = VLayout<DP>::VL, VR = VLayout<DP>::VR, NS = VLayout<DP>::NS;
@@ -529,6 +531,10 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
             const uint16_t *vb = a.v + off;
 #pragma unroll
             for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kb + (col * tok32 + kd[c]));
+            if constexpr (MASK) {   // tokens past t1 read the group's first token's byte (in bounds)
+                const int tk = gs + col < x.t1 ? gs + col : gs;
+                r.keep = a.mask[(int64_t)x.s * a.mask_stride + tk];
+            }
             // uniform row pointer per step, one lane offset for all steps
 #pragma unroll
             for (int i = 0; i < NS; ++i) ld_v<VE>(vb + (int64_t)(VR * i) * a.tok + vlane, r.v[i]);
@@ -546,6 +552,7 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
             const uint16_t *kp = a.k + ((int64_t)bk * a.blk + gk + (int64_t)(tk - pk * a.bs) * a.tok);
 #pragma unroll
             for (int c = 0; c < NCK; ++c) r.k[c] = ld16(kp + kd[c]);
+            if constexpr (MASK) r.keep = a.mask[(int64_t)x.s * a.mask_stride + tk];
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const int tv = gs + VR * i + vr < x.t1 ? gs + VR * i + vr : gs;
@@ -576,7 +583,8 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
         for (int c = 0; c < NCK; ++c)
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.q[c]),
                                                            __builtin_bit_cast(bf16x8, r.k[c]), sacc, 0, 0, 0);
-        const bool valid = gs + col < x.t1;
+        const bool valid = gs + col < x.t1 && (!MASK || r.keep != 0);
+        if constexpr (MASK) r.kept = __builtin_amdgcn_ballot_w64(valid);
         float sc[4], rm[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc[i] = valid ? sacc[i] * a.scale_log2 : -INFINITY;
@@ -611,9 +619,16 @@ __global__ void __launch_bounds__(kThreads) attend_kernel(const AttendArgs a) {
 
     auto pv = [&](const Item<DP> &x, GroupRegs<DP> &r, int n) {
         const int gs = x.t0 + 16 * n;
-        // the last group may hold rows past t1: zero their V so that
-        // 0 * (NaN or Inf) never reaches the sums
-        if (gs + 16 > x.t1) {
+        // rows that take no part (past t1, or dropped by the mask) get V = 0,
+        // so that 0 * (NaN or Inf) never reaches the sums
+        if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                const bool ok = (r.kept >> (VR * i + vr)) & 1;
+#pragma unroll
+                for (int e = 0; e < VE / 2; ++e) r.v[i][e] = ok ? r.v[i][e] : 0u;
+            }
+        } else if (gs + 16 > x.t1) {
 #pragma unroll
             for (int i = 0; i < NS; ++i) {
                 const bool ok = gs + VR * i + vr < x.t1;
@@ -976,9 +991,9 @@ __global__ void __launch_bounds__(256) finalize_kernel(const float *l, const flo
 // two for head dim 256 (measured faster there: 16 KB per group).
 constexpr int nbuf_for(int dp) { return dp == 256 ? 2 : 4; }
 
-template <int DP, int GC, bool P16, bool TILE>
+template <int DP, int GC, bool P16, bool TILE, bool MASK>
 hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
-    auto kernel = attend_kernel<DP, GC, P16, nbuf_for(DP), TILE>;
+    auto kernel = attend_kernel<DP, GC, P16, nbuf_for(DP), TILE, MASK>;
     const size_t dyn = a.prefix_mode ? 2 * sizeof(int) * ((size_t)a.S + 1) : 0;
     // One workgroup (four waves) per compute unit: measured on MI355X, the
     // paged row streams of one wave per SIMD reach a higher HBM rate than two
@@ -1004,12 +1019,15 @@ hipError_t launch_attend_t(const AttendArgs &a, int cus, hipStream_t st, const A
 
 template <int DP, int GC>
 hipError_t launch_attend_p(const Plan &p, const AttendArgs &a, int cus, hipStream_t st, const AttendEvents &ev) {
-    const bool tile = a.out == nullptr;
-    if (p.p16)
-        return tile ? launch_attend_t<DP, GC, true, true>(a, cus, st, ev)
-                    : launch_attend_t<DP, GC, true, false>(a, cus, st, ev);
-    return tile ? launch_attend_t<DP, GC, false, true>(a, cus, st, ev)
-                : launch_attend_t<DP, GC, false, false>(a, cus, st, ev);
+    const bool tile = a.out == nullptr;   // the kv mask comes with decode only
+    if (p.p16) {
+        if (tile) return launch_attend_t<DP, GC, true, true, false>(a, cus, st, ev);
+        return a.mask ? launch_attend_t<DP, GC, true, false, true>(a, cus, st, ev)
+                      : launch_attend_t<DP, GC, true, false, false>(a, cus, st, ev);
+    }
+    if (tile) return launch_attend_t<DP, GC, false, true, false>(a, cus, st, ev);
+    return a.mask ? launch_attend_t<DP, GC, false, false, true>(a, cus, st, ev)
+                  : launch_attend_t<DP, GC, false, false, false>(a, cus, st, ev);
 }
 
 template <int DP>

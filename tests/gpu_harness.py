@@ -103,14 +103,20 @@ class Device:
             t.fill_(fill - 0x10000 if fill >= 0x8000 else fill)   # uint16 bit pattern
         return t
 
-    def decode(self, tile=0, bps=0, out=None, ws=None, use_lastv_array=True, lv_default=None):
+    def decode(self, tile=0, bps=0, out=None, ws=None, use_lastv_array=True, lv_default=None,
+               mask=None):
+        """pda_decode, or pda_decode_masked when a host keep-mask [S, width] is given."""
         p = self.p
         out = self.new_out(0x7FC0) if out is None else out
         ws = self.workspace(bps) if ws is None else ws
-        self.pda.pda_decode(self.dims(), self.q, self.kp, self.vp, self.blocks[tile],
-                            self.counts[tile], self.lastv[tile] if use_lastv_array else None,
-                            p.bs if lv_default is None else lv_default, p.S, p.strides, ws, out,
-                            bps)
+        args = (self.dims(), self.q, self.kp, self.vp, self.blocks[tile], self.counts[tile],
+                self.lastv[tile] if use_lastv_array else None,
+                p.bs if lv_default is None else lv_default, p.S, p.strides)
+        if mask is None:
+            self.pda.pda_decode(*args, ws, out, bps)
+        else:
+            m = self.torch.from_numpy(np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))).to(self.dev)
+            self.pda.pda_decode_masked(*args, m, m.shape[1], ws, out, bps)
         return out
 
     def new_state(self):

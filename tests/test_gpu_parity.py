@@ -298,6 +298,119 @@ def test_many_sequences_both_enumerations(S):
         assert_parity(out_to_f64(out), ref, label=f"S={S} tiled bps={bps}")
 
 
+def oracle_masked(dev: Device, mask):
+    p = dev.p
+    return oracle.attend(p.q, p.pool, p.k_base, p.v_base, p.strides, p.Hkv, p.bs, p.blocks[:1],
+                         p.counts[:1], p.lastv[:1], mask=mask)
+
+
+def _mask(rng, ctx, width, p_drop):
+    m = rng.random((len(ctx), width)) >= p_drop
+    if len(ctx) > 1:
+        m[-1, :] = False                  # one sequence keeps nothing
+    return m
+
+
+@pytest.mark.parametrize("shape", [s for s in SMALL if s[7] == 1],
+                         ids=lambda s: "x".join(map(str, s[:5])) + f"-{s[6]}")
+@pytest.mark.parametrize("bps", [0, 1, 3])
+def test_masked_decode_small_shapes(shape, bps):
+    """pda_decode_masked against the oracle with the same keep-mask: ragged
+    masks (30 % dropped), one sequence fully dropped (all-zero row)."""
+    S, Hq, Hkv, D, bs, ctx, layout, T = shape
+    announce("masked small", shape, "bps", bps)
+    rng = np.random.Generator(np.random.PCG64(hash((S, Hq, D, bs, 99)) % (1 << 32)))
+    case = build_case(rng, S, Hq, Hkv, D, bs, ctx, layout=layout)
+    dev = Device(case)
+    mask = _mask(rng, ctx, max(ctx) + 5, 0.3)
+    ref = oracle_masked(dev, mask)["out"]
+    got = out_to_f64(dev.decode(bps=bps, mask=mask))
+    assert_parity(got, ref, label=f"masked {shape} bps {bps}")
+    if S > 1:
+        assert np.all(out_bits(dev.decode(bps=bps, mask=mask))[-1] == 0)
+
+
+def test_masked_positions_never_read_into_the_result():
+    """Tokens whose K and V are NaN and whose mask bytes drop them leave the
+    output finite and equal to the oracle's (which skips them); an all-keep
+    mask gives the unmasked kernel's bits."""
+    announce("masked poison")
+    rng = np.random.Generator(np.random.PCG64(81))
+    ctx = [40, 73, 9]
+    bad = [set(rng.choice(c, size=max(1, c // 5), replace=False).tolist()) for c in ctx]
+
+    def values(s, T):
+        k = rng.standard_normal((T, 2, 64))
+        v = rng.standard_normal((T, 2, 64))
+        for t in bad[s]:
+            k[t] = np.nan
+            v[t] = np.nan
+        return k, v
+
+    case = build_case(rng, 3, 8, 2, 64, 16, ctx, values=values)
+    dev = Device(case)
+    mask = np.ones((3, 80), dtype=bool)
+    for s in range(3):
+        for t in bad[s]:
+            mask[s, t] = False
+    ref = oracle_masked(dev, mask)["out"]
+    for bps in (0, 1):
+        got = out_to_f64(dev.decode(bps=bps, mask=mask))
+        assert np.all(np.isfinite(got))
+        assert_parity(got, ref, label=f"masked NaN tokens bps {bps}")
+    clean = build_case(np.random.Generator(np.random.PCG64(82)), 2, 8, 2, 64, 16, [50, 17])
+    dc = Device(clean)
+    np.testing.assert_array_equal(out_bits(dc.decode(mask=np.ones((2, 64), bool))),
+                                  out_bits(dc.decode()))
+
+
+@pytest.mark.parametrize("use_mask", [False, True])
+def test_attn_paged_decode_token_granular(use_mask):
+    """The blhd wrapper with token-granular tables (block size 1, as the pages'
+    backend calls its paged decode), against the oracle."""
+    import torch
+    announce("attn_paged_decode bs=1 mask", use_mask)
+    rng = np.random.Generator(np.random.PCG64(83))
+    S, Hq, Hkv, D = 4, 8, 2, 128
+    ctx = [1, 57, 300, 129]
+    case = build_case(rng, S, Hq, Hkv, D, 1, ctx)
+    dev = Device(case)
+    mask = _mask(rng, ctx, 320, 0.25) if use_mask else None
+    ref = (oracle_masked(dev, mask) if use_mask else oracle_of(dev))["out"]
+    p = dev.p
+    nblk = p.v_base // (Hkv * D)     # K pages, then V pages, block size 1
+    kc = dev.pool[p.k_base:p.k_base + nblk * Hkv * D].view(torch.bfloat16).view(nblk, 1, Hkv, D)
+    vc = dev.pool[p.v_base:p.v_base + nblk * Hkv * D].view(torch.bfloat16).view(nblk, 1, Hkv, D)
+    q = dev.q.view(torch.bfloat16).view(S, 1, Hq, D)
+    lens = torch.tensor(ctx, dtype=torch.int32)
+    m = None if mask is None else torch.from_numpy(mask)
+    out = pda_mod().attn_paged_decode(q, kc, vc, dev.blocks[0], lens, mask=m)
+    got = out_to_f64(out.view(torch.int16)).reshape(S, Hq, D)
+    assert_parity(got, ref, label=f"wrapper mask={use_mask}")
+
+
+def pda_mod():
+    import paged_gqa_decode_pda_amd as pda
+    return pda
+
+
+def test_masked_full_size_llama3_sampled():
+    """The llama3-8b-b16 workload with a random keep-mask (10 % dropped), in
+    the benchmark's launch configuration, on sampled rows."""
+    announce("masked full-size llama3-8b-b16")
+    w = workloads.named("llama3-8b-b16")
+    dev = Device(w)
+    rng = np.random.default_rng(84)
+    width = int(max(w.contexts)) + 8
+    mask = rng.random((w.num_seqs, width)) >= 0.1
+    pairs = np.unique(rng.choice(w.num_seqs * w.num_q_heads, size=96, replace=False))
+    b, c, v = w.stacked_tiles()
+    ref = oracle.attend(w.q, w.pool, w.k_base, w.v_base, w.strides, w.num_kv_heads, w.block_size,
+                        b, c, v, pairs=pairs, mask=mask)
+    got = out_to_f64(dev.decode(mask=mask)).reshape(-1, w.head_dim)[pairs]
+    assert_parity(got, ref["out"], label="masked llama3-8b-b16")
+
+
 def test_workspace_reuse_across_calls():
     """One workspace serves many calls with different data and split counts:
     the work counters a call leaves behind must be zero and no call may read

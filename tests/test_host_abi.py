@@ -225,3 +225,37 @@ def test_debug_time_attention_arming():
         pda.pda_debug_time_attention(None, FAKE)
     pda.pda_debug_time_attention(FAKE, FAKE + 64)
     pda.pda_debug_time_attention(None, None)
+
+
+def test_decode_masked_validation_before_enqueue():
+    """pda_decode_masked rejects a NULL mask and a non-positive row stride
+    before anything is enqueued (addresses are never dereferenced)."""
+    d = dims()
+    common = dict(q=FAKE, k_pool=FAKE, v_pool=FAKE, block_tables=FAKE, block_counts=FAKE,
+                  last_block_valid=FAKE, last_block_valid_default=16, num_seqs=2,
+                  strides=pda.pda_paged_strides(d), workspace=FAKE, out=FAKE,
+                  workspace_bytes=pda.pda_workspace_bytes(d), stream=0)
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_decode_masked(d, **common, kv_mask=None, mask_stride=64)
+    assert e.value.status == pda.PDA_ERR_NULL
+    for stride in (0, -5):
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_decode_masked(d, **common, kv_mask=FAKE, mask_stride=stride)
+        assert e.value.status == pda.PDA_ERR_DIMS
+    with pytest.raises(pda.PdaError) as e:   # the ordinary checks still apply
+        pda.pda_decode_masked(d, **{**common, "num_seqs": 99}, kv_mask=FAKE, mask_stride=64)
+    assert e.value.status == pda.PDA_ERR_MAX_SEQS
+
+
+def test_attn_paged_decode_rejects_host_tensors():
+    """The blhd convenience wrapper refuses host tensors and wrong shapes
+    before any library call."""
+    import torch
+    q = torch.zeros(2, 1, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(8, 1, 2, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    lens = torch.tensor([3, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pda.attn_paged_decode(q, kc, kc, bt, lens)
+    with pytest.raises(ValueError):
+        pda.attn_paged_decode(q[:, 0], kc, kc, bt, lens)
