@@ -6,7 +6,10 @@ imports, links or runs anything here, and this package imports nothing from
 the GPU library.
 
 ``attend`` wraps the plain C definition in ``pda_oracle.c`` (two passes over
-each gathered token list, binary64 throughout); ``merge`` is the log-sum-exp
+each gathered token list, binary64 throughout); ``prefill`` is the same
+definition for a chunk of queries per sequence, each keeping the keys up to
+its own position when causal (AstrAI "CUDA Kernels", "Python Wrappers":
+is_causal and the [batch, q_len, kv_len] mask); ``merge`` is the log-sum-exp
 fold of two (m, l, o) running states.  The operation follows the AstrAI
 "CUDA Kernels" page (section "Python Wrappers": blhd layout, scale
 1/sqrt(head_dim)) and the spark_storage "tiled_attention.rs" page (header
@@ -51,6 +54,10 @@ def load_library(path):
                                       i64, i32, i32, P, P, P, P, i64, P, i64, P, P, P, P,
                                       ctypes.c_int]
     lib.pda_oracle_attend.restype = ctypes.c_int
+    lib.pda_oracle_prefill.argtypes = [i32, i32, i32, i32, i32, i32, P, P, i64, i64, i64, i64,
+                                       i64, i64, i32, P, P, P, i32, P, i64, i64, P, i64, P, P,
+                                       P, P, ctypes.c_int]
+    lib.pda_oracle_prefill.restype = ctypes.c_int
     return lib
 
 
@@ -154,6 +161,72 @@ def attend_workload(w, tiles=None, pairs=None, threads=None):
         b, c, v = b[:tiles], c[:tiles], v[:tiles]
     return attend(w.q, w.pool, w.k_base, w.v_base, w.strides, w.num_kv_heads, w.block_size,
                   b, c, v, pairs=pairs, threads=threads)
+
+
+def prefill(q, pool, k_base, v_base, strides, num_kv_heads, block_size, blocks, counts,
+            last_valid, causal=True, mask=None, rows=None, threads=None, lib=None):
+    """Attention of a chunk of q_len queries per sequence over its listed tokens.
+
+    q           uint16 [S, q_len, Hq, D] bf16 bits; the queries are the newest
+                q_len tokens of their sequence, so query i of a sequence listing
+                P tokens sits at position P - q_len + i
+    blocks      int32 [S, capacity];  counts, last_valid int32 [S]
+    causal      keep only keys at positions up to the query's own
+    mask        optional bool/uint8 [S, q_len, kv_len] (or [S, kv_len], shared by
+                the chunk's queries): key t is kept for query i where true
+    rows        optional int array of (s * q_len + i) * Hq + h to evaluate
+
+    Returns m, l ([n] or [S, q_len, Hq]) and o, out ([n, D] or [S, q_len, Hq, D]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    S, Q, Hq, D = q.shape
+    pool = np.ascontiguousarray(pool, dtype=np.uint16).reshape(-1)
+    blocks = np.ascontiguousarray(np.asarray(blocks, dtype=np.int32))
+    counts = np.ascontiguousarray(np.asarray(counts, dtype=np.int32).reshape(S))
+    last_valid = np.ascontiguousarray(np.asarray(last_valid, dtype=np.int32).reshape(S))
+    assert blocks.ndim == 2 and blocks.shape[0] == S
+    cap = blocks.shape[1]
+    if rows is None:
+        n, rows_arr = S * Q * Hq, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+        n = rows_arr.size
+    m = np.empty(n, np.float64)
+    l = np.empty(n, np.float64)
+    o = np.empty((n, D), np.float64)
+    out = np.empty((n, D), np.float64)
+    blk, tok, kvh = (int(x) for x in strides)
+    ss = qs = 0
+    if mask is not None:
+        mask = np.ascontiguousarray(np.asarray(mask).astype(np.uint8))
+        assert mask.shape[0] == S and mask.ndim in (2, 3)
+        if mask.ndim == 3:
+            assert mask.shape[1] == Q
+            ss, qs = mask.shape[1] * mask.shape[2], mask.shape[2]
+        else:
+            ss, qs = mask.shape[1], 0
+        total = _listed_tokens(counts[None], last_valid[None], cap, int(block_size))
+        assert np.all(total <= mask.shape[-1]), "the mask must cover every listed position"
+    rc = (lib or _load()).pda_oracle_prefill(
+        S, Q, Hq, int(num_kv_heads), D, int(block_size), q.ctypes.data, pool.ctypes.data,
+        pool.size, int(k_base), int(v_base), blk, tok, kvh, cap, blocks.ctypes.data,
+        counts.ctypes.data, last_valid.ctypes.data, 1 if causal else 0,
+        None if mask is None else mask.ctypes.data, ss, qs,
+        None if rows_arr is None else rows_arr.ctypes.data, n, m.ctypes.data, l.ctypes.data,
+        o.ctypes.data, out.ctypes.data, int(threads or host_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its inputs (code {rc})")
+    if rows is None:
+        return {"m": m.reshape(S, Q, Hq), "l": l.reshape(S, Q, Hq), "o": o.reshape(S, Q, Hq, D),
+                "out": out.reshape(S, Q, Hq, D)}
+    return {"m": m, "l": l, "o": o, "out": out}
+
+
+def prefill_workload(w, causal=True, mask=None, rows=None, threads=None):
+    """`prefill` over a prefill workload object (one tile, its chunk queries)."""
+    b, c, v = w.stacked_tiles()
+    return prefill(w.qc, w.pool, w.k_base, w.v_base, w.strides, w.num_kv_heads, w.block_size,
+                   b[0], c[0], v[0], causal=causal, mask=mask, rows=rows, threads=threads)
 
 
 def merge(a, b):

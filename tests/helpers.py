@@ -49,6 +49,15 @@ class Case:
     seq_pages: List[np.ndarray]
     num_pages: int
     tile_token_ranges: list  # per tile, per sequence: (t_lo, t_hi) logical token range
+    qc: Optional[np.ndarray] = None    # uint16 [S, q_len, Hq, D]: prefill chunk queries
+    qcf: Optional[np.ndarray] = None   # float64, the same values
+
+    def prefill_args(self):
+        """Arguments of oracle.prefill (one tile, the chunk queries)."""
+        assert self.qc is not None and self.blocks.shape[0] == 1
+        return dict(q=self.qc, pool=self.pool, k_base=self.k_base, v_base=self.v_base,
+                    strides=self.strides, num_kv_heads=self.Hkv, block_size=self.bs,
+                    blocks=self.blocks[0], counts=self.counts[0], last_valid=self.last_valid[0])
 
     def oracle_args(self):
         return dict(q=self.q, pool=self.pool, k_base=self.k_base, v_base=self.v_base,
@@ -185,4 +194,52 @@ def dense_reference(case: Case, tiles: Optional[int] = None, mask=None):
             am = torch.from_numpy(keep).view(1, 1, 1, hi - lo)
         o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am)
         out[s] = o[0, :, 0, :].numpy()
+    return out
+
+
+def prefill_case(rng: np.random.Generator, S, Q, Hq, Hkv, D, bs, contexts, qc_values=None,
+                 **kw) -> Case:
+    """build_case (one tile) plus a chunk of Q queries per sequence, N(0, 1)
+    unless qc_values [S, Q, Hq, D] is given."""
+    case = build_case(rng, S, Hq, Hkv, D, bs, contexts, **kw)
+    qv = rng.standard_normal((S, Q, Hq, D)) if qc_values is None else np.asarray(qc_values, np.float64)
+    case.qc = to_bits(qv).reshape(S, Q, Hq, D)
+    case.qcf = bf16_round(qv).reshape(S, Q, Hq, D)
+    return case
+
+
+def dense_prefill_reference(case: Case, keep=None, sdpa_causal=False):
+    """Chunk attention over the dense logical rows with torch's float64 CPU
+    scaled_dot_product_attention (GQA by repeat_interleave).  keep(s) -> bool
+    [Q, T_s] is handed to the routine as its attn_mask (rows keeping nothing
+    are left 0 here); sdpa_causal=True uses the routine's own is_causal
+    instead (which aligns query i with key i)."""
+    import torch
+    S, Q = case.qc.shape[:2]
+    G = case.Hq // case.Hkv
+    out = np.zeros((S, Q, case.Hq, case.D))
+    for s in range(S):
+        T = case.K[s].shape[0]
+        if T == 0:
+            continue
+        k = torch.from_numpy(case.K[s]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        v = torch.from_numpy(case.V[s]).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        q = torch.from_numpy(case.qcf[s]).permute(1, 0, 2)          # [Hq, Q, D]
+        k, v, q = (x.unsqueeze(0).contiguous() for x in (k, v, q))
+        if sdpa_causal:
+            o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+            out[s] = o[0].permute(1, 0, 2).numpy()
+            continue
+        am = None
+        rows = np.ones(Q, dtype=bool)
+        if keep is not None:
+            km = np.asarray(keep(s), dtype=bool)[:, :T]
+            rows = km.any(axis=1)
+            km = km.copy()
+            km[~rows] = True         # any finite row; zeroed below
+            am = torch.from_numpy(km).view(1, 1, Q, T)
+        o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=am)
+        o = o[0].permute(1, 0, 2).numpy()
+        o[~rows] = 0.0
+        out[s] = o
     return out

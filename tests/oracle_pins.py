@@ -14,7 +14,8 @@ import os
 
 import numpy as np
 
-from helpers import bf16_round, build_case, dense_reference, to_bits
+from helpers import (bf16_round, build_case, dense_prefill_reference, dense_reference,
+                     prefill_case, to_bits)
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -319,3 +320,126 @@ ALL_PINS = [pin_context_one, pin_identical_keys, pin_zero_query, pin_page_permut
             pin_dense_library, pin_poison, pin_key_shift, pin_linear_in_v, pin_peaked,
             pin_golden_closed_form, pin_mask_dense_library, pin_mask_is_removal,
             pin_mask_all_keep]
+
+
+# ---------------------------------------------------------------------------
+# Prefill: a chunk of q_len queries per sequence (the newest q_len tokens of
+# the sequence, whose keys are already listed).  Each pin below takes a
+# ``prefill`` callable with the signature of ``oracle.prefill`` (and, where a
+# pin reduces to decode, an ``attend`` callable too).
+
+PREFILL_SHAPES = [
+    # S, Q, Hq, Hkv, D, bs, contexts, layout
+    (2, 5, 4, 2, 16, 4, [5, 5], "paged"),
+    (3, 7, 8, 2, 8, 3, [7, 7, 7], "scratch"),
+    (1, 16, 2, 1, 32, 16, [16], "paged"),
+    (2, 4, 6, 3, 8, 1, [4, 4], "scratch"),
+]
+
+
+def pin_prefill_square_library_causal(prefill, attend=None):
+    """With as many queries as listed tokens the chunk is the whole sequence,
+    and causal attention is torch's float64 scaled_dot_product_attention with
+    its own is_causal switch (library routine; at q_len = kv_len its alignment
+    and the chunk's coincide)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    for S, Q, Hq, Hkv, D, bs, ctx, layout in PREFILL_SHAPES:
+        case = prefill_case(rng, S, Q, Hq, Hkv, D, bs, ctx, layout=layout)
+        r = prefill(**case.prefill_args(), causal=True)
+        np.testing.assert_allclose(r["out"], dense_prefill_reference(case, sdpa_causal=True),
+                                   rtol=0, atol=1e-12, err_msg=f"{(S, Q, Hq, Hkv, D, bs, ctx)}")
+
+
+def pin_prefill_causal_is_tril(prefill, attend=None):
+    """Causal attention of a chunk equals non-causal attention under the
+    lower-triangular keep pattern np.tril(ones(q_len, P), k=P - q_len) (a
+    library routine for the diagonal offset of a chunk that ends the sequence),
+    and both equal torch's scaled_dot_product_attention with that pattern as
+    attn_mask; ragged contexts, P < q_len (queries keeping nothing give 0 and
+    l = 0) and an empty sequence included."""
+    rng = np.random.Generator(np.random.PCG64(32))
+    for S, Q, Hq, Hkv, D, bs, ctx, layout in [
+            (3, 4, 4, 2, 16, 4, [11, 4, 2], "paged"),
+            (2, 6, 8, 1, 8, 5, [23, 0], "scratch"),
+            (2, 3, 2, 2, 24, 1, [9, 3], "paged")]:
+        case = prefill_case(rng, S, Q, Hq, Hkv, D, bs, ctx, layout=layout)
+        W = max(ctx) + 2
+        tri = np.zeros((S, Q, W), dtype=bool)
+        for s in range(S):
+            tri[s, :, :ctx[s]] = np.tril(np.ones((Q, ctx[s]), dtype=bool), k=ctx[s] - Q)
+        a = prefill(**case.prefill_args(), causal=True)
+        b = prefill(**case.prefill_args(), causal=False, mask=tri)
+        for key in ("m", "l", "o", "out"):
+            np.testing.assert_array_equal(a[key], b[key])
+        want = dense_prefill_reference(case, keep=lambda s: tri[s])
+        np.testing.assert_allclose(a["out"], want, rtol=0, atol=1e-12)
+        for s in range(S):
+            for i in range(Q):
+                if ctx[s] - Q + i < 0:
+                    assert np.all(a["l"][s, i] == 0.0) and np.all(a["out"][s, i] == 0.0)
+
+
+def pin_prefill_future_keys(prefill, attend=None):
+    """Changing the key and value at position p changes exactly the chunk
+    queries at positions >= p and leaves every earlier query bit for bit
+    unchanged (causality, with the query's own position included)."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    S, Q, Hq, Hkv, D, bs, P = 1, 6, 4, 2, 8, 4, 10
+    base = prefill_case(rng, S, Q, Hq, Hkv, D, bs, [P])
+    a = prefill(**base.prefill_args(), causal=True)
+    for p in range(P - Q - 1, P):
+        K = [base.K[0].copy()]
+        V = [base.V[0].copy()]
+        K[0][p] += 3.0
+        V[0][p] -= 5.0
+        case = prefill_case(np.random.Generator(np.random.PCG64(34)), S, Q, Hq, Hkv, D, bs, [P],
+                            values=lambda s, T: (K[s], V[s]), qc_values=base.qcf)
+        b = prefill(**case.prefill_args(), causal=True)
+        for i in range(Q):
+            pos = P - Q + i
+            same = np.array_equal(a["out"][0, i], b["out"][0, i])
+            assert same == (pos < p), f"position {p}, query {i}"
+
+
+def pin_prefill_noncausal_is_decode(prefill, attend):
+    """Without the causal switch every chunk query sees every listed key, so
+    query i equals single-token decode of that query over the same pages, bit
+    for bit; and with q_len = 1 causal prefill is decode too."""
+    rng = np.random.Generator(np.random.PCG64(35))
+    case = prefill_case(rng, 2, 3, 8, 2, 16, 4, [13, 6], layout="scratch")
+    r = prefill(**case.prefill_args(), causal=False)
+    for i in range(3):
+        d = attend(**{**case.oracle_args(), "q": case.qc[:, i]})
+        for key in ("m", "l", "o", "out"):
+            np.testing.assert_array_equal(r[key][:, i], d[key])
+    one = prefill(**{**case.prefill_args(), "q": case.qc[:, 2:3]}, causal=True)
+    d = attend(**{**case.oracle_args(), "q": case.qc[:, 2]})
+    for key in ("m", "l", "o", "out"):
+        np.testing.assert_array_equal(one[key][:, 0], d[key])
+
+
+def pin_prefill_mask_library(prefill, attend=None):
+    """A [batch, q_len, kv_len] keep-mask ([CK] Python Wrappers) without the
+    causal switch is torch's scaled_dot_product_attention with that boolean
+    attn_mask; a [batch, kv_len] mask equals the 3D mask with every query row
+    the same, bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(36))
+    S, Q, Hq, Hkv, D, bs, ctx = 3, 5, 4, 2, 16, 4, [14, 7, 20]
+    case = prefill_case(rng, S, Q, Hq, Hkv, D, bs, ctx)
+    m3 = rng.random((S, Q, 21)) >= 0.35
+    m3[0, 2] = False             # one query keeps nothing
+    r = prefill(**case.prefill_args(), causal=False, mask=m3)
+    np.testing.assert_allclose(r["out"], dense_prefill_reference(case, keep=lambda s: m3[s]),
+                               rtol=0, atol=1e-12)
+    assert np.all(r["l"][0, 2] == 0.0) and np.all(r["out"][0, 2] == 0.0)
+    m2 = rng.random((S, 21)) >= 0.35
+    a = prefill(**case.prefill_args(), causal=True, mask=m2)
+    b = prefill(**case.prefill_args(), causal=True,
+                mask=np.broadcast_to(m2[:, None, :], (S, Q, 21)))
+    for key in ("m", "l", "o", "out"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+PREFILL_PINS = [pin_prefill_square_library_causal, pin_prefill_causal_is_tril,
+                pin_prefill_future_keys, pin_prefill_noncausal_is_decode,
+                pin_prefill_mask_library]

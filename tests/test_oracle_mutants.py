@@ -11,7 +11,10 @@ import oracle_pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "pda_oracle.c")
 
 MUTANTS = {
-    "gqa_map_modulo": ("const int32_t g = h / G;", "const int32_t g = h % num_kv_heads;"),
+    "gqa_map_modulo": ("(sh % num_q_heads);\n            const int32_t g = h / G;",
+                       "(sh % num_q_heads);\n            const int32_t g = h % num_kv_heads;"),
+    "prefill_gqa_modulo": ("(si % q_len);\n            const int32_t g = h / G;",
+                           "(si % q_len);\n            const int32_t g = h % num_kv_heads;"),
     "last_page_full": ("if (i == cnt - 1)", "if (0)"),
     "last_valid_short": ("for (int32_t j = 0; j < valid; ++j)",
                          "for (int32_t j = 0; j < valid - 1; ++j)"),
@@ -19,16 +22,23 @@ MUTANTS = {
     "no_max_shift": ("double w = exp(score[t] - M);", "double w = exp(score[t]);"),
     "sign_flip": ("double w = exp(score[t] - M);", "double w = exp(M - score[t]);"),
     "strides_swapped": ("(int64_t)j * tok + (int64_t)g * kvh", "(int64_t)j * kvh + (int64_t)g * tok"),
-    "v_from_k": ("pool + v_base + rows[t]", "pool + k_base + rows[t]"),
+    "v_from_k": ("vpool + rows[t]", "kpool + rows[t]"),
     "dot_skips_d0": ("for (int32_t d = 0; d < head_dim; ++d) acc +=",
                      "for (int32_t d = 1; d < head_dim; ++d) acc +="),
     "no_normalise": ("L > 0.0 ? op[d] / L : 0.0", "L > 0.0 ? op[d] : 0.0"),
-    "first_tile_only": ("for (int32_t t = 0; t < n_tiles; ++t)", "for (int32_t t = 0; t < 1; ++t)"),
-    "mask_ignored": ("mask[(int64_t)s * mask_stride + pos] != 0", "1"),
-    "mask_inverted": ("mask[(int64_t)s * mask_stride + pos] != 0", "mask[(int64_t)s * mask_stride + pos] == 0"),
+    "first_tile_only": ("capacity);\n        const int32_t *list", "capacity);\n        if (t > 0) break;\n        const int32_t *list"),
+    "mask_ignored": ("mask_row[pos] != 0", "1"),
+    "mask_inverted": ("mask_row[pos] != 0", "mask_row[pos] == 0"),
     "mask_position_per_page": ("                ++pos;\n", ""),
     "q_head_swapped": ("q + ((int64_t)s * num_q_heads + h) * head_dim",
                        "q + ((int64_t)s * num_q_heads + (num_q_heads - 1 - h)) * head_dim"),
+    "prefill_causal_strict": ("causal ? P - q_len + i :", "causal ? P - q_len + i - 1 :"),
+    "prefill_top_left": ("causal ? P - q_len + i :", "causal ? (int64_t)i :"),
+    "prefill_causal_ignored": ("causal ? P - q_len + i : INT64_MAX", "INT64_MAX"),
+    "prefill_q_layout": ("q + (si * num_q_heads + h) * head_dim",
+                         "q + (((int64_t)s * num_q_heads + h) * q_len + i) * head_dim"),
+    "prefill_mask_query_shared": ("(int64_t)i * mask_q_stride", "(int64_t)0 * mask_q_stride"),
+    "prefill_mask_seq_shared": ("mask + (int64_t)s * mask_seq_stride", "mask + (int64_t)0 * mask_seq_stride"),
 }
 
 
@@ -47,6 +57,9 @@ def test_mutant_fails_a_pin(name, tmp_path):
     def attend(**kw):
         return oracle.attend(**kw, lib=lib)
 
+    def prefill(**kw):
+        return oracle.prefill(**kw, lib=lib)
+
     failed = []
     for pin in oracle_pins.ALL_PINS:
         try:
@@ -57,4 +70,9 @@ def test_mutant_fails_a_pin(name, tmp_path):
         oracle_pins.pin_tiled_merge(attend, oracle.merge)
     except (AssertionError, ValueError):
         failed.append("pin_tiled_merge")
+    for pin in oracle_pins.PREFILL_PINS:
+        try:
+            pin(prefill, attend)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"

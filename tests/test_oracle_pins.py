@@ -11,6 +11,26 @@ def test_pin(pin):
     pin(oracle.attend)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PREFILL_PINS, ids=lambda f: f.__name__)
+def test_prefill_pin(pin):
+    pin(oracle.prefill, oracle.attend)
+
+
+def test_prefill_rows_subset_matches_full():
+    """A sample of (sequence, query, head) rows gives the same bits as the full
+    evaluation (the sampled mode used at full workload sizes)."""
+    from helpers import prefill_case
+    rng = np.random.Generator(np.random.PCG64(37))
+    case = prefill_case(rng, 2, 5, 4, 2, 8, 4, [12, 3])
+    full = oracle.prefill(**case.prefill_args())
+    rows = np.array([39, 0, 17, 8, 21])
+    part = oracle.prefill(**case.prefill_args(), rows=rows)
+    for key in ("m", "l"):
+        np.testing.assert_array_equal(part[key], full[key].reshape(-1)[rows])
+    for key in ("o", "out"):
+        np.testing.assert_array_equal(part[key], full[key].reshape(-1, 8)[rows])
+
+
 def test_tiled_merge_pin():
     oracle_pins.pin_tiled_merge(oracle.attend, oracle.merge)
 

@@ -37,7 +37,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsynth.so")
 BF16_NAN = 0x7FC0
 
-STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
+STREAM_Q, STREAM_K, STREAM_V, STREAM_QC = 1, 2, 3, 4
 
 _lib = None
 
@@ -131,6 +131,12 @@ class Workload:
     tiles: List[Tile]
     tile_capacity: int
     seed: int = 0
+    qc: Optional[np.ndarray] = None  # uint16 [S, q_len, Hq, D]: a prefill chunk's queries
+    q_len: int = 1
+
+    @property
+    def is_prefill(self) -> bool:
+        return self.qc is not None
 
     @property
     def gqa(self) -> int:
@@ -152,6 +158,25 @@ class Workload:
         D, S = self.head_dim, self.num_seqs
         return (4 * self.num_kv_heads * D * self.total_tokens
                 + 2 * S * self.num_q_heads * D * 2)
+
+    def prefill_keys(self, causal: bool = True) -> np.ndarray:
+        """int64 [S, q_len]: keys each chunk query attends to (no mask).  Query i
+        of a sequence of P tokens sits at position P - q_len + i."""
+        P = self.contexts.astype(np.int64)[:, None]
+        if not causal:
+            return np.broadcast_to(P, (self.num_seqs, self.q_len)).copy()
+        i = np.arange(self.q_len, dtype=np.int64)[None, :]
+        return np.clip(P - self.q_len + i + 1, 0, P)
+
+    def prefill_flops(self, causal: bool = True) -> int:
+        """Multiply-adds x 2 of q.K^T and P.V over the kept keys."""
+        return int(self.prefill_keys(causal).sum()) * self.num_q_heads * 4 * self.head_dim
+
+    def prefill_bytes(self) -> int:
+        """K+V bytes of the listed tokens plus the chunk's q and output bytes."""
+        D = self.head_dim
+        return (4 * self.num_kv_heads * D * self.total_tokens
+                + 2 * self.num_seqs * self.q_len * self.num_q_heads * D * 2)
 
     def row_start(self, base: int, block: int, slot: int, kv_head: int) -> int:
         blk, tok, kvh = self.strides
@@ -327,6 +352,17 @@ def make_workload(*, name: str, seed: int, num_seqs: int, num_q_heads: int, num_
                     tile_capacity=cap, seed=seed)
 
 
+def make_prefill(*, q_len: int, **kw) -> Workload:
+    """A workload whose sequences end in a chunk of q_len new query tokens (their
+    keys already in the cache): the cache as `make_workload` builds it, plus
+    chunk queries ``qc`` [S, q_len, Hq, D] from their own generator stream."""
+    w = make_workload(**kw)
+    n = w.num_seqs * q_len * w.num_q_heads * w.head_dim
+    w.qc = normal_bf16(w.seed, STREAM_QC, n).reshape(w.num_seqs, q_len, w.num_q_heads, w.head_dim)
+    w.q_len = int(q_len)
+    return w
+
+
 # The named workloads: name -> (seed, description).
 WORKLOADS = {
     "tiny": (1001, "S=1 Hq/Hkv=4/1 D=64 bs=16 ctx=100 paged, one tile"),
@@ -334,6 +370,9 @@ WORKLOADS = {
     "ragged-b64": (1003, "S=64 Hq/Hkv=32/8 D=128 bs=16 ctx~logU[128,32768] paged, 1% keys x4"),
     "wide-head-d256": (1004, "S=4 Hq/Hkv=16/8 D=256 bs=16 ctx=65536 paged, 8 tiles of 512 pages"),
     "scratch-b256": (1005, "S=256 Hq/Hkv=32/8 D=128 bs=16 ctx~U[2048,8192] scratch, 4 tiles"),
+    "prefill-2048": (1006, "prefill S=1 q_len=2048 ctx=2048 Hq/Hkv=32/8 D=128 bs=16 paged, causal"),
+    "prefill-chunk-b16": (1007, "prefill S=16 q_len=256 ctx~U[512,4096] Hq/Hkv=32/8 D=128 bs=16 "
+                                "paged, causal"),
 }
 
 
@@ -362,6 +401,15 @@ def named(name: str) -> Workload:
         return make_workload(name=name, seed=seed, num_seqs=4, num_q_heads=16,
                              num_kv_heads=8, head_dim=256, block_size=16,
                              contexts=[65536] * 4, n_tiles=8, tile_capacity=512, rng=rng)
+    if name == "prefill-2048":
+        return make_prefill(q_len=2048, name=name, seed=seed, num_seqs=1, num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16, contexts=[2048],
+                            tile_capacity=128, rng=rng)
+    if name == "prefill-chunk-b16":
+        ctx = rng.integers(512, 4096, endpoint=True, size=16)
+        return make_prefill(q_len=256, name=name, seed=seed, num_seqs=16, num_q_heads=32,
+                            num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
+                            tile_capacity=256, rng=rng)
     ctx = rng.integers(2048, 8192, endpoint=True, size=256)
     return make_workload(name=name, seed=seed, num_seqs=256, num_q_heads=32,
                          num_kv_heads=8, head_dim=128, block_size=16, contexts=ctx,
