@@ -19,7 +19,8 @@
  *        wrappers fail loudly when the compiled library is absent), section
  *        "Attention Backend" (decode through the paged kernel with page
  *        size 1) and the "Overview" table (GQA decode with split-KV; paged
- *        KV-cache decode).
+ *        KV-cache decode; GQA prefill), the is_causal switch and the
+ *        [batch, q_len, kv_len] mask of "Python Wrappers" for prefill.
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
@@ -206,11 +207,58 @@ pda_status pda_decode_masked(const pda_dims *dims, const void *q, const void *k_
                              void *workspace, size_t workspace_bytes, void *out,
                              int32_t blocks_per_split, void *stream);
 
+/* Device workspace bytes for pda_prefill with chunks of q_len queries and the
+ * given blocks_per_split (0 = the library's choice, sized for any device):
+ * the fp32 split partials of max_seqs * q_len * num_q_heads rows, slots =
+ * ceil(tile_capacity / bps) each, (m, l) pairs then o rows,
+ * rows * slots * (head_dim + 2) * 4 + 16 bytes; 0 when no call with these
+ * sizes splits (one split covers tile_capacity pages), and 0 if dims are
+ * invalid or q_len < 1.  Needs no clearing; calls sharing a workspace must
+ * not run concurrently. */
+size_t pda_prefill_workspace_bytes(const pda_dims *dims, int32_t q_len, int32_t blocks_per_split);
+
+/* Prefill / chunked prefill ([CK] Overview: GQA prefill; Python Wrappers:
+ * is_causal and the [batch, q_len, kv_len] mask; Attention Backend: prefill
+ * next to decode).  Each sequence brings a chunk of q_len query tokens that
+ * are its newest tokens, their keys and values already written to the pages
+ * it lists: query i of a sequence listing P tokens sits at position
+ * P - q_len + i.
+ *   dims, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+ *   last_block_valid_default, num_seqs, strides   as pda_decode
+ *   q_len         queries per sequence, >= 1 (PDA_ERR_DIMS otherwise)
+ *   q             device bf16 [num_seqs, q_len, num_q_heads, head_dim] (blhd)
+ *   causal        non-zero: query i keeps keys at positions 0 .. P - q_len + i
+ *                 (none if that is negative); zero: every listed key
+ *   kv_mask       NULL, or device uint8: key t takes part for query i of
+ *                 sequence s only where kv_mask[s * mask_seq_stride +
+ *                 i * mask_q_stride + t] != 0 (mask_q_stride 0 shares one
+ *                 [batch, kv_len] row across the chunk), on top of causal;
+ *                 strides >= 0 (PDA_ERR_DIMS otherwise)
+ *   workspace     device, pda_prefill_workspace_bytes(dims, q_len,
+ *                 blocks_per_split) bytes (may be NULL when that is 0)
+ *   out           device bf16 [num_seqs, q_len, num_q_heads, head_dim]
+ *   blocks_per_split  pages per split-KV partition, 0 = the library's choice
+ *   rows_per_wave     16, 32 or 64 query rows (q_len x q-head pairs of one kv
+ *                 head) per wavefront, 0 = the library's choice; capped at 16
+ *                 for head_dim > 128 and at 32 for head_dim > 64 with a mask
+ * q head h attends with kv head h / (num_q_heads / num_kv_heads), scale
+ * 1/sqrt(head_dim).  A query that keeps no key gets an all-zero row.
+ * Device-side contract as pda_decode; with a mask, every row covers the
+ * tokens its sequence lists. */
+pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const void *k_pool,
+                       const void *v_pool, const int32_t *block_tables,
+                       const int32_t *block_counts, const int32_t *last_block_valid,
+                       int32_t last_block_valid_default, int32_t num_seqs, pda_strides strides,
+                       int32_t causal, const uint8_t *kv_mask, int64_t mask_seq_stride,
+                       int64_t mask_q_stride, void *workspace, size_t workspace_bytes, void *out,
+                       int32_t blocks_per_split, int32_t rows_per_wave, void *stream);
+
 /* Timing diagnostics, for benchmarks that need the attention kernel's own
- * duration: arms the calling thread's next pda_decode or pda_step_tile call
- * to record `before` and `after` (hipEvent_t handles owned by the caller,
- * passed as void*) on that call's stream right before and right after its
- * attention kernel, ahead of the split merge.  The next call that launches
+ * duration: arms the calling thread's next pda_decode, pda_decode_masked,
+ * pda_step_tile or pda_prefill call to record `before` and `after`
+ * (hipEvent_t handles owned by the caller, passed as void*) on that call's
+ * stream right before and right after its attention kernel, ahead of the
+ * split merge.  The next call that launches
  * the attention kernel consumes the pair; NULL, NULL disarms.  PDA_ERR_NULL
  * if exactly one of them is NULL. */
 pda_status pda_debug_time_attention(void *before, void *after);

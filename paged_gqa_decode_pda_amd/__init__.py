@@ -42,7 +42,7 @@ EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_bl
             "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
             "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
             "pda_step_tile", "pda_finalize", "pda_decode", "pda_decode_masked",
-            "pda_debug_time_attention",
+            "pda_prefill_workspace_bytes", "pda_prefill", "pda_debug_time_attention",
             "pda_status_string", "pda_last_error"]
 
 
@@ -95,6 +95,9 @@ _sig("pda_decode", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_st
      _P, _i32, _P)
 _sig("pda_decode_masked", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P,
      _i64, _P, _sz, _P, _i32, _P)
+_sig("pda_prefill_workspace_bytes", _sz, _PD, _i32, _i32)
+_sig("pda_prefill", ctypes.c_int, _PD, _i32, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _i32,
+     _P, _i64, _i64, _P, _sz, _P, _i32, _i32, _P)
 _sig("pda_debug_time_attention", ctypes.c_int, _P, _P)
 _sig("pda_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("pda_last_error", ctypes.c_char_p)
@@ -263,6 +266,88 @@ def pda_decode_masked(dims, q, k_pool, v_pool, block_tables, block_counts, last_
                                   _stream(stream)))
 
 
+def pda_prefill_workspace_bytes(dims, q_len: int, blocks_per_split: int = 0) -> int:
+    d = _dims(dims)
+    return _lib.pda_prefill_workspace_bytes(ctypes.byref(d), q_len, blocks_per_split)
+
+
+def pda_prefill(dims, q_len: int, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                last_block_valid_default: int, num_seqs: int, strides, causal: bool, kv_mask,
+                mask_seq_stride: int, mask_q_stride: int, workspace, out,
+                blocks_per_split: int = 0, rows_per_wave: int = 0, stream=None,
+                workspace_bytes=None) -> None:
+    d = _dims(dims)
+    nb = _nbytes(workspace) if workspace_bytes is None else int(workspace_bytes)
+    _check(_lib.pda_prefill(ctypes.byref(d), int(q_len), _addr(q), _addr(k_pool), _addr(v_pool),
+                            _addr(block_tables), _addr(block_counts), _addr(last_block_valid),
+                            last_block_valid_default, num_seqs, _strides(strides),
+                            1 if causal else 0, _addr(kv_mask), int(mask_seq_stride),
+                            int(mask_q_stride), _addr(workspace), nb, _addr(out),
+                            blocks_per_split, rows_per_wave, _stream(stream)))
+
+
+def _paged_args(q, k_cache, v_cache, block_table, seq_lens):
+    """Checks of the pages' wrapper convention and the C-ABI arguments derived
+    from it: (dims, strides, block_table, counts, last_valid)."""
+    import torch
+    B, _, Hq, D = q.shape
+    nblk, bs, Hkv, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, n_kv_heads, head_dim]")
+    for t in (q, k_cache, v_cache):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError("q, k_cache and v_cache must be contiguous bfloat16 tensors")
+        if t.device.type != "cuda":
+            raise ValueError("q, k_cache and v_cache must be device tensors")
+    if block_table.device.type != "cuda":
+        raise ValueError("block_table must be a device tensor")
+    block_table = block_table.to(torch.int32).contiguous()
+    cap = block_table.shape[1]
+    lens = seq_lens.to(device=block_table.device, dtype=torch.int32)
+    counts = ((lens + (bs - 1)) // bs).to(torch.int32).contiguous()
+    lastv = torch.where(counts > 0, lens - (counts - 1) * bs, torch.zeros_like(lens)).to(torch.int32).contiguous()
+    dims = pda_dims(B, Hq, Hkv, D, bs, cap)
+    return dims, pda_paged_strides(dims), block_table, counts, lastv
+
+
+def attn_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, is_causal: bool = True,
+                       mask=None, out=None, workspace=None, blocks_per_split: int = 0,
+                       rows_per_wave: int = 0, stream=None):
+    """Prefill attention in the pages' wrapper convention: q [batch, q_len,
+    n_heads, head_dim] bf16 (blhd), the chunk's keys already in k_cache /
+    v_cache [num_blocks, block_size, n_kv_heads, head_dim] as the newest q_len
+    of seq_lens[b] tokens; is_causal as the pages' switch; mask optional bool
+    [batch, kv_len] or [batch, q_len, kv_len] (True = keep).  Returns out
+    [batch, q_len, n_heads, head_dim] bf16.  Argument derivation and
+    allocation only; the attention runs in the library's kernels."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, q_len, n_heads, head_dim]")
+    B, Q, Hq, D = q.shape
+    if mask is not None and seq_lens.device.type == "cpu" and seq_lens.numel() and \
+            int(seq_lens.max()) > mask.shape[-1]:
+        raise ValueError("mask rows are shorter than the longest sequence")
+    dims, strides, block_table, counts, lastv = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
+    bs = dims.block_size
+    if out is None:
+        out = torch.empty((B, Q, Hq, D), dtype=torch.bfloat16, device=q.device)
+    if workspace is None:
+        nb = pda_prefill_workspace_bytes(dims, Q, blocks_per_split)
+        workspace = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=q.device)
+    m, ss, qs = None, 0, 0
+    if mask is not None:
+        m = mask.to(device=q.device, dtype=torch.uint8).contiguous()
+        if m.dim() == 2 and m.shape[0] == B:
+            ss, qs = m.shape[1], 0
+        elif m.dim() == 3 and m.shape[0] == B and m.shape[1] == Q:
+            ss, qs = m.shape[1] * m.shape[2], m.shape[2]
+        else:
+            raise ValueError("mask must be [batch, kv_len] or [batch, q_len, kv_len]")
+    pda_prefill(dims, Q, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
+                is_causal, m, ss, qs, workspace, out, blocks_per_split, rows_per_wave, stream)
+    return out
+
+
 def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, mask=None, out=None,
                       workspace=None, blocks_per_split: int = 0, stream=None):
     """Decode attention in the calling convention of the pages' paged decode
@@ -279,26 +364,11 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, mask=None, out
     if q.dim() != 4 or q.shape[1] != 1:
         raise ValueError("q must be [batch, 1, n_heads, head_dim]")
     B, _, Hq, D = q.shape
-    nblk, bs, Hkv, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k_cache and v_cache must both be [num_blocks, block_size, n_kv_heads, head_dim]")
-    for t in (q, k_cache, v_cache):
-        if t.dtype != torch.bfloat16 or not t.is_contiguous():
-            raise ValueError("q, k_cache and v_cache must be contiguous bfloat16 tensors")
-        if t.device.type != "cuda":
-            raise ValueError("q, k_cache and v_cache must be device tensors")
-    if block_table.device.type != "cuda":
-        raise ValueError("block_table must be a device tensor")
     if mask is not None and seq_lens.device.type == "cpu" and seq_lens.numel() and \
             int(seq_lens.max()) > mask.shape[-1]:
         raise ValueError("mask rows are shorter than the longest sequence")
-    block_table = block_table.to(torch.int32).contiguous()
-    cap = block_table.shape[1]
-    lens = seq_lens.to(device=block_table.device, dtype=torch.int32)
-    counts = ((lens + (bs - 1)) // bs).to(torch.int32).contiguous()
-    lastv = torch.where(counts > 0, lens - (counts - 1) * bs, torch.zeros_like(lens)).to(torch.int32).contiguous()
-    dims = pda_dims(B, Hq, Hkv, D, bs, cap)
-    strides = pda_paged_strides(dims)
+    dims, strides, block_table, counts, lastv = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
+    bs = dims.block_size
     if out is None:
         out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=q.device)
     if workspace is None:

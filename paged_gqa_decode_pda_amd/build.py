@@ -12,12 +12,12 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpda.so")
-SOURCES = [os.path.join(HERE, "csrc", "pda_api.hip"), os.path.join(HERE, "csrc", "pda_kernels.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("pda_api.hip", "pda_kernels.hip", "pda_prefill.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every HIP translation unit; hipcc's
 # host pass warns that it does not know the feature, which is harmless.
-HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include"),
              # single-lane work-queue claims: keep the compiler from turning
@@ -33,11 +33,25 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra=()) -> str:
+    """Compiles every source to an object in parallel, then links libpda.so."""
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(HERE, "csrc", os.path.basename(src) + ".o")
+        cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+        objs.append(obj)
+    failed = [p.args[-1] for p in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {failed}")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

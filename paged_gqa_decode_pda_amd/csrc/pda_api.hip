@@ -75,11 +75,6 @@ int device_cus() {
     return cus;
 }
 
-// Pages per split.  An explicit request is clamped to [1, tile_capacity].
-// Otherwise tile_capacity / 128 rounded to a power of two and clamped to
-// [8, 64] pages (never below ceil(tile_capacity / 256)): long page lists get
-// longer splits, so that a sequence's split count, and with it the combine
-// work, stays bounded.
 // Events armed by pda_debug_time_attention for this thread's next launch.
 thread_local pda::AttendEvents t_events;
 
@@ -89,11 +84,13 @@ pda::AttendEvents take_events() {
     return ev;
 }
 
+// Pages per split.  An explicit request is clamped to [1, tile_capacity].
+// Otherwise splits of about 256 tokens, never more than 256 per sequence.
 int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
     (void)num_seqs;
     const int32_t cap = d->tile_capacity;
     if (request > 0) return request > cap ? cap : request;
-    // splits of about 256 tokens (16 groups of 16), and at most 256 per sequence
+    // splits of about 256 tokens (16 groups of 16)
     int32_t bps = 256 / d->block_size;
     if (bps < 1) bps = 1;
     if (bps < min_auto_bps(d)) bps = min_auto_bps(d);
@@ -101,10 +98,6 @@ int32_t resolve_bps(const pda_dims *d, int32_t request, int32_t num_seqs) {
     return bps;
 }
 
-// Partial slots per sequence for splits of bps pages.  Up to kPrefixMaxSeqs
-// sequences the kernel groups about 3/4 of a sequence's splits four at a
-// time, so a sequence with n splits has n - 3 * floor(3n / 16) slots;
-// beyond that every split has its own slot.
 // Partial slots one (sequence, q head) row can need: one per item.  A
 // sequence of n splits has n items when every split is an item, and
 // n - (big - 1) * floor(e n / (8 big)) with big items (never more), so n
@@ -405,6 +398,131 @@ pda_status pda_decode_masked(const pda_dims *dims, const void *q, const void *k_
     return decode_impl(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
                        last_block_valid_default, num_seqs, strides, kv_mask, mask_stride, workspace,
                        workspace_bytes, out, blocks_per_split, stream);
+}
+
+namespace {
+
+constexpr int32_t kPrefillMinSplitTokens = 256;
+
+int padded_dim(int D) { return D <= 64 ? 64 : (D <= 128 ? 128 : 256); }
+
+// Pages per prefill split: the request clamped to [1, tile_capacity]; else
+// whole page lists when the (sequence, kv head, row tile) items already give
+// every SIMD a wave, otherwise about enough splits to do so, each of at
+// least kPrefillMinSplitTokens tokens.
+int32_t prefill_bps(const pda_dims *d, int32_t request, int64_t items, int cus) {
+    const int32_t cap = d->tile_capacity;
+    if (request > 0) return request > cap ? cap : request;
+    const int64_t want = 4LL * cus;
+    const int32_t min_bps = (int32_t)ceil_div(kPrefillMinSplitTokens, d->block_size);
+    if (items >= want || min_bps >= cap) return cap;
+    const int64_t nsp = ceil_div(want, items);
+    int32_t bps = (int32_t)ceil_div(cap, nsp);
+    if (bps < min_bps) bps = min_bps;
+    return bps > cap ? cap : bps;
+}
+
+int32_t prefill_nsplit(const pda_dims *d, int32_t bps) { return (int32_t)ceil_div(d->tile_capacity, bps); }
+
+size_t prefill_workspace_for(const pda_dims *d, int32_t q_len, int32_t bps) {
+    const int32_t ns = prefill_nsplit(d, bps);
+    if (ns <= 1) return 0;
+    // (m, l) pairs, padded to 16 bytes, then the o rows
+    return (size_t)d->max_seqs * q_len * d->num_q_heads * ns * (d->head_dim + 2) * sizeof(float) + 16;
+}
+
+}  // namespace
+
+size_t pda_prefill_workspace_bytes(const pda_dims *d, int32_t q_len, int32_t request) {
+    if (check_dims(d) != PDA_OK || q_len < 1) return 0;
+    const int32_t min_bps = (int32_t)ceil_div(kPrefillMinSplitTokens, d->block_size);
+    int32_t bps = request > 0 ? request : min_bps;
+    if (bps > d->tile_capacity) bps = d->tile_capacity;
+    return prefill_workspace_for(d, q_len, bps);
+}
+
+pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const void *k_pool,
+                       const void *v_pool, const int32_t *block_tables,
+                       const int32_t *block_counts, const int32_t *last_block_valid,
+                       int32_t last_block_valid_default, int32_t num_seqs, pda_strides strides,
+                       int32_t causal, const uint8_t *kv_mask, int64_t mask_seq_stride,
+                       int64_t mask_q_stride, void *workspace, size_t workspace_bytes, void *out,
+                       int32_t blocks_per_split, int32_t rows_per_wave, void *stream) {
+    clear_err();
+    pda_status st = check_dims(dims);
+    if (st != PDA_OK) return st;
+    if (num_seqs < 0 || num_seqs > dims->max_seqs)
+        return fail(PDA_ERR_MAX_SEQS, "num_seqs %d outside [0, max_seqs=%d]", num_seqs, dims->max_seqs);
+    const int G = dims->num_q_heads / dims->num_kv_heads;
+    if (q_len < 1 || (int64_t)q_len * G > (int64_t(1) << 24))
+        return fail(PDA_ERR_DIMS, "q_len %d outside [1, 2^24 / gqa_ratio]", q_len);
+    if (blocks_per_split < 0) return fail(PDA_ERR_DIMS, "blocks_per_split must be >= 0");
+    if (rows_per_wave != 0 && rows_per_wave != 16 && rows_per_wave != 32 && rows_per_wave != 64)
+        return fail(PDA_ERR_DIMS, "rows_per_wave must be 0, 16, 32 or 64");
+    if ((st = check_tile_ptrs(q, k_pool, v_pool, block_tables, block_counts, last_block_valid)) != PDA_OK)
+        return st;
+    if (!out) return fail(PDA_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if ((st = check_strides(dims, strides)) != PDA_OK) return st;
+    if (kv_mask && (mask_seq_stride < 0 || mask_q_stride < 0))
+        return fail(PDA_ERR_DIMS, "mask strides must be >= 0");
+    if (workspace && !aligned(workspace, 16))
+        return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (num_seqs == 0) return PDA_OK;
+
+    const int dp = padded_dim(dims->head_dim);
+    int rb = rows_per_wave / 16;
+    const int max_rb = pda::prefill_max_rb(dp, kv_mask != nullptr);
+    if (rb == 0) {   // the fewest row blocks that cover a kv head's rows, within the instantiated shapes
+        const int64_t rows = (int64_t)q_len * G;
+        rb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+    }
+    if (rb > max_rb) rb = max_rb;
+    const int32_t ntiles = (int32_t)ceil_div((int64_t)q_len * G, 16 * rb);
+    const int cus = device_cus();
+    const int64_t items = (int64_t)num_seqs * dims->num_kv_heads * ntiles;
+    const int32_t bps = prefill_bps(dims, blocks_per_split, items, cus);
+    const int32_t nsplit = prefill_nsplit(dims, bps);
+    if ((int64_t)num_seqs * nsplit * dims->num_kv_heads * ntiles > (int64_t(1) << 31) - 4096)
+        return fail(PDA_ERR_DIMS, "too many work items");
+    const size_t need = prefill_workspace_for(dims, q_len, bps);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+
+    pda::PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k_pool);
+    a.v = static_cast<const uint16_t *>(v_pool);
+    a.blocks = block_tables;
+    a.counts = block_counts;
+    a.lastv = last_block_valid;
+    a.mask = kv_mask;
+    a.mask_ss = kv_mask ? mask_seq_stride : 0;
+    a.mask_qs = kv_mask ? mask_q_stride : 0;
+    a.out = static_cast<uint16_t *>(out);
+    a.part_ml = static_cast<float *>(workspace);
+    const int64_t ml_floats = ((int64_t)num_seqs * q_len * dims->num_q_heads * nsplit * 2 + 3) / 4 * 4;
+    a.part_o = a.part_ml ? a.part_ml + ml_floats : nullptr;
+    a.blk = strides.blk;
+    a.tok = strides.tok;
+    a.kvh = strides.kvh;
+    a.bs_magic = ((uint64_t(1) << 32) + (uint64_t)dims->block_size - 1) / (uint64_t)dims->block_size;
+    a.S = num_seqs;
+    a.Q = q_len;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.G = G;
+    a.D = dims->head_dim;
+    a.bs = dims->block_size;
+    a.cap = dims->tile_capacity;
+    a.lv_default = last_block_valid_default;
+    a.span = bps * dims->block_size;
+    a.nsplit = nsplit;
+    a.ntiles = ntiles;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
+    hipError_t e = pda::launch_prefill(a, dp, rb, static_cast<hipStream_t>(stream), take_events());
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "prefill launch");
 }
 
 pda_status pda_debug_time_attention(void *before, void *after) {

@@ -77,6 +77,36 @@ struct AttendEvents {
 
 hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st,
                          const AttendEvents &ev);
+
+// Prefill: a chunk of Q query tokens per sequence (the sequence's newest
+// tokens), rows (i, h) of kv head g ordered r = i G + (h - g G).
+struct PrefillArgs {
+    const uint16_t *q;        // bf16 [S, Q, Hq, D]
+    const uint16_t *k;        // bf16 K pool base
+    const uint16_t *v;        // bf16 V pool base
+    const int32_t *blocks;    // int32 [S, cap] page ids
+    const int32_t *counts;    // int32 [S]
+    const int32_t *lastv;     // int32 [S] or null
+    const uint8_t *mask;      // keep-mask, byte (s, i, t) at s mask_ss + i mask_qs + t, or null
+    int64_t mask_ss, mask_qs;
+    uint16_t *out;            // bf16 [S, Q, Hq, D]
+    float *part_ml;           // fp32 [S Q Hq, nsplit, 2]: (m in log2 units, l) per split
+    float *part_o;            // fp32 [S Q Hq, nsplit, D]
+    int64_t blk, tok, kvh;    // strides in bf16 elements
+    uint64_t bs_magic;        // ceil(2^32 / bs)
+    int32_t S, Q, Hq, Hkv, G, D, bs, cap, lv_default;
+    int32_t span;             // tokens per kv split (a whole number of pages)
+    int32_t nsplit;           // split slots per sequence: ceil(cap bs / span)
+    int32_t ntiles;           // row tiles per kv head: ceil(Q G / (16 rb))
+    int32_t causal;
+    float scale_log2;         // log2(e) / sqrt(D)
+};
+
+// dp: padded head dim (64, 128, 256); rb: 16-row blocks per wave (1, 2, 4,
+// at most prefill_max_rb(dp, with a mask)).  Launches the attention kernel,
+// then the split merge when nsplit > 1.
+int prefill_max_rb(int dp, bool mask);
+hipError_t launch_prefill(const PrefillArgs &a, int dp, int rb, hipStream_t st, const AttendEvents &ev);
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st);
 hipError_t launch_finalize(const float *l, const float *o, uint16_t *out, int64_t rows, int D,
                            hipStream_t st);

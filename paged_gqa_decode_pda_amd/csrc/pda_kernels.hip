@@ -31,35 +31,13 @@
 //      lane%16) holds elements [c*D_PAD/16, (c+1)*D_PAD/16) of token 4i + r.
 //      Softmax weights move from the score layout to the V layout through LDS.
 #include "pda_internal.h"
-
+#include "pda_device.h"
 
 namespace pda {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.69314718055994531f;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-
-// The two bf16 halves of a dword, widened exactly to fp32.
-__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-// DPP lane permutations (all source lanes valid for the controls used).
-constexpr int kRowRor4 = 0x124;   // row_ror:4 (within 16-lane rows)
-constexpr int kRowRor8 = 0x128;   // row_ror:8
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Control words shared across XCDs (the work counter, rewound for the next
 // launch; the item sizing, passed to the merge kernel) are written with
@@ -72,29 +50,6 @@ __device__ __forceinline__ void st_coherent_i(int *p, int v) {
 __device__ __forceinline__ int ld_coherent_i(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0): this wave's vector memory operations completed
-
-// Lanes of one wave exchange data through LDS: make prior LDS writes visible
-// to the wave's other lanes before the reads that follow.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// binary32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
-
-__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
-__device__ __forceinline__ u32x2 ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
-
-
 
 // VE / 2 dwords of bf16 pairs (VE = 2 or 4 elements) of a V row.  V rows
 // are streamed once per call and each load covers whole cache lines, so they
@@ -146,10 +101,6 @@ __device__ __forceinline__ int seq_tokens(const int32_t *counts, const int32_t *
     if (cnt == 0) return 0;
     int lv = clampi(lastv ? lastv[s] : lv_default, 0, bs);
     return (cnt - 1) * bs + lv;
-}
-
-__device__ __forceinline__ int page_of(uint32_t t, uint64_t magic) {
-    return (int)(((uint64_t)t * magic) >> 32);
 }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

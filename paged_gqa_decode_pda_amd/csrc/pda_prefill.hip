@@ -1,0 +1,546 @@
+// gfx950 (CDNA4) kernels for paged grouped-query prefill: a chunk of q_len
+// query tokens per sequence, the sequence's newest tokens (their keys already
+// in the paged cache), attends over the sequence's listed tokens.  Query i of
+// a sequence listing P tokens sits at position P - q_len + i; with the causal
+// switch it keeps keys up to its own position, and an optional keep-mask
+// [batch, q_len, kv_len] removes positions on top of that (AstrAI "CUDA
+// Kernels": the "Overview" table's prefill kernel, section "Python Wrappers"
+// for is_causal, the mask and the blhd layout, section "Attention Backend"
+// for prefill next to decode).
+//
+// With q_len * G query rows per kv head the scores are a dense contraction,
+// so both products run on v_mfma_f32_16x16x32_bf16:
+//   scores, transposed: S^T (16 tokens x 16 rows) = K (A operand, 16 token
+//      rows loaded straight from the pages) x Q^T (B operand, the q rows).
+//      Lane l gets rows l%16 and tokens 4(l/16) + i, i = 0..3, so two
+//      16-token halves leave lane l exactly the 8 weights that the B operand
+//      of the next product needs from row l%16: no transpose of P.
+//   output, transposed: O^T (16 head-dim elements x 16 rows) += V^T (A
+//      operand) x P^T (B operand), 32 tokens deep, with the 32 tokens taken in
+//      the order (4(l/16) .. +3 of half 0, the same of half 1) that the
+//      scores left in the lanes.  V^T's lanes need 8 tokens of one column,
+//      so each 32-token V tile goes through LDS (row-major, 16-byte writes,
+//      2-byte transposed reads on a padded pitch that keeps the four lane
+//      groups on disjoint banks).  O^T's lanes hold row l%16, so the online
+//      softmax rescale of a row never leaves its lane.
+//
+// Work items: (sequence, kv split, kv head, row tile) with the row tile
+// fastest; a wave takes one item (RB row blocks of 16 query rows, rows
+// r = i * G + (h - g G) of kv head g) and streams the split's tokens in steps
+// of 32, one step of loads ahead.  Workgroups are renumbered so that
+// consecutive items, which read the same pages, run on one XCD (one L2).
+// A sequence whose tokens fit one split gets its bf16 result directly;
+// otherwise each item leaves (m, l, o) partials for prefill_merge_kernel.
+#include <type_traits>
+
+#include "pda_internal.h"
+#include "pda_device.h"
+
+namespace pda {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = 64 * kPfWaves;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS pitch (bytes) of one V row: 16 bytes of padding shift every fourth row
+// by 16 banks.
+template <int DP>
+struct PfTile {
+    static constexpr int kPitch = 2 * DP + 16;
+    static constexpr int kBytes = 32 * kPitch;
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to a bf16 pair, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// The running max a row's weights are taken against moves only when the
+// row's true max exceeds it by more than this (log2 units): weights stay
+// below 2^kRescaleSlack, and the rescale of the accumulators is rare.
+constexpr float kRescaleSlack = 8.f;
+
+// Maximum of x over the four lanes l, l^16, l^32, l^48 (one row of the
+// transposed scores).
+__device__ __forceinline__ float max4(float x) {
+    x = fmaxf(x, shfl_xor(x, 16));
+    return fmaxf(x, shfl_xor(x, 32));
+}
+__device__ __forceinline__ float sum4(float x) {
+    x += shfl_xor(x, 16);
+    return x + shfl_xor(x, 32);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = max(x, __shfl_xor(x, m, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = min(x, __shfl_xor(x, m, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+    return x;
+}
+
+// Tokens sequence s lists: its first `cnt` pages, all full except the last.
+__device__ __forceinline__ int seq_tokens_pf(const PrefillArgs &a, int s) {
+    const int cnt = clampi(a.counts[s], 0, a.cap);
+    if (cnt == 0) return 0;
+    return (cnt - 1) * a.bs + clampi(a.lastv ? a.lastv[s] : a.lv_default, 0, a.bs);
+}
+
+__device__ __forceinline__ int or16(int x) {   // OR over the 16 lanes of a row
+    x |= __shfl_xor(x, 1, 64);
+    x |= __shfl_xor(x, 2, 64);
+    x |= __shfl_xor(x, 4, 64);
+    return x | __shfl_xor(x, 8, 64);
+}
+
+// 16-byte load at a byte offset (under 2^32) from a wave-uniform base, so the
+// address is a scalar base plus a 32-bit lane offset.
+__device__ __forceinline__ u32x4 ld16_at(const uint16_t *base, uint32_t byte_off) {
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+template <int DP, int RB, bool MASK, bool P16>
+__global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a) {
+    constexpr int NCK = DP / 32;          // 32-element chunks of the head dim
+    constexpr int NDB = DP / 16;          // 16-element blocks of the head dim (output)
+    constexpr int CPR = DP / 8;           // 16-byte chunks per V row
+    constexpr int RPI = 64 / CPR;         // V rows per load instruction
+    constexpr int NV = 32 / RPI;          // V load instructions per 32-token step
+    constexpr int PITCH = PfTile<DP>::kPitch;
+    __shared__ __attribute__((aligned(16))) unsigned char vt_all[kPfWaves][PfTile<DP>::kBytes];
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qd = lane >> 4, col = lane & 15;
+    unsigned char *vt = vt_all[w];
+
+    // XCD-aware numbering: hardware workgroup b runs on XCD b % 8, so the
+    // logical index groups consecutive items on one XCD (the grid is a
+    // multiple of 8).
+    const int nwg = (int)gridDim.x, b = (int)blockIdx.x;
+    const int lwg = (b & 7) * (nwg >> 3) + (b >> 3);
+    const int64_t item = (int64_t)lwg * kPfWaves + w;
+    const int64_t nitems = (int64_t)a.S * a.nsplit * a.Hkv * a.ntiles;
+    if (item >= nitems) return;
+    const int rt = (int)(item % a.ntiles);
+    int64_t rest = item / a.ntiles;
+    const int g = (int)(rest % a.Hkv);
+    rest /= a.Hkv;
+    const int sp = (int)(rest % a.nsplit);
+    const int s = (int)(rest / a.nsplit);
+
+    const int P = seq_tokens_pf(a, s);
+    const int span = a.span;
+    const int nsp = P > 0 ? (P + span - 1) / span : 0;
+    if (sp >= (nsp > 0 ? nsp : 1)) return;
+    const bool direct = nsp <= 1;
+
+    // this lane's rows, one per row block: r = rt 16 RB + 16 b + col
+    const int QG = a.Q * a.G;
+    int lim[RB];            // last key position the row keeps (-1: none)
+    int64_t rowid[RB];      // (s Q + i) Hq + h, or -1 past the chunk
+    const uint8_t *mrow[RB];  // the row's keep-mask bytes (with a mask)
+    int lim_max = -1, lim_min = 0x7fffffff;
+    u32x4 qb[RB][NCK];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = rt * 16 * RB + 16 * rb + col;
+        const bool ok = r < QG;
+        const int i = ok ? r / a.G : 0;
+        const int h = g * a.G + (ok ? r - i * a.G : 0);
+        rowid[rb] = ok ? ((int64_t)s * a.Q + i) * a.Hq + h : -1;
+        lim[rb] = ok ? (a.causal ? P - a.Q + i : P - 1) : -1;
+        mrow[rb] = MASK ? a.mask + (int64_t)s * a.mask_ss + (int64_t)i * a.mask_qs : nullptr;
+        lim_max = max(lim_max, lim[rb]);
+        if (ok) lim_min = min(lim_min, lim[rb]);
+        const uint16_t *qp = a.q + (ok ? rowid[rb] : 0) * a.D;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) {
+            const int d0 = 32 * c + 8 * qd;
+            qb[rb][c] = (ok && d0 < a.D) ? ld16(qp + d0) : u32x4{0, 0, 0, 0};
+        }
+    }
+    lim_max = __builtin_amdgcn_readfirstlane(wave_max_i(lim_max));
+    lim_min = __builtin_amdgcn_readfirstlane(wave_min_i(lim_min));
+
+    const int t0 = sp * span;
+    const int t1 = min(min(t0 + span, P), lim_max + 1);
+    const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+
+    float m2[RB], lsum[RB];
+    f32x4_t acc[RB][NDB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m2[rb] = -INFINITY;
+        lsum[rb] = 0.f;
+#pragma unroll
+        for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int32_t *brow = a.blocks + (int64_t)s * a.cap;
+    const int64_t gk = (int64_t)g * a.kvh;
+    int cb = t0 / a.bs;   // first page of the page-id window
+    int bidvec = brow[min(cb + lane, a.cap - 1)];
+    int kd[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) {
+        const int d0 = 32 * c + 8 * qd;
+        kd[c] = d0 < a.D ? d0 : 0;   // past head_dim: re-read chunk 0 (q is 0 there)
+    }
+    const int vrow = lane / CPR;           // V row within a load instruction
+    const int vd = (lane % CPR) * 8;       // first V element of the lane
+    const int vdo = vd < a.D ? vd : 0;
+    // lane byte offsets from a page row's start, for steps whose 16-token
+    // halves each lie inside one page (block_size a multiple of 16)
+    uint32_t kob[NCK];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c) kob[c] = 2u * (uint32_t)(col * (int)a.tok + kd[c]);
+    const uint32_t vob = 2u * (uint32_t)(vrow * (int)a.tok + vdo);
+    // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
+    // 16-aligned and listed
+    auto half_base = [&](int tb, int hf) -> int64_t {
+        const int th = tb + 16 * hf;
+        const int pg = page_of((uint32_t)th, a.bs_magic);
+        const int bid = __builtin_amdgcn_readlane(bidvec, pg - cb);
+        return (int64_t)bid * a.blk + gk + (int64_t)(th - pg * a.bs) * a.tok;
+    };
+
+    // Element offset of token t's row (kv head g); t must be listed.
+    auto row_of = [&](int t) -> int64_t {
+        const int pg = page_of((uint32_t)t, a.bs_magic);
+        const int bid = __shfl(bidvec, pg - cb, 64);
+        return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
+    };
+
+    // K of two steps in flight (double-buffered registers); V of the next
+    // step is requested as soon as the current one is in LDS.
+    u32x4 kr[2][2][NCK];   // [buffer][half][chunk]
+    u32x4 vr[NV];
+    auto issue_k = [&](int st, int buf) {
+        const int tb = t0 + 32 * st;
+        const int last = min(tb + 31, t1 - 1);
+        if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {   // move the window
+            cb = page_of((uint32_t)tb, a.bs_magic);
+            bidvec = brow[min(cb + lane, a.cap - 1)];
+            // wait here, so that the path without a move carries no wait
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+        if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint16_t *kb = a.k + half_base(tb, hf);
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) kr[buf][hf][c] = ld16_at(kb, kob[c]);
+            }
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
+                const uint16_t *kp = a.k + row_of(t);
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) kr[buf][hf][c] = ld16(kp + kd[c]);
+            }
+        }
+    };
+    auto issue_v = [&](int st) {
+        const int tb = t0 + 32 * st;
+        if (P16 && tb + 32 <= t1) {
+            const uint16_t *vb[2] = {a.v + half_base(tb, 0), a.v + half_base(tb, 1)};
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
+                vr[v] = ld16_at(vb[hf] + (int64_t)r0 * a.tok, vob);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int t = min(tb + RPI * v + vrow, t1 - 1);
+                vr[v] = ld16(a.v + row_of(t) + vdo);
+            }
+        }
+    };
+
+    auto compute = [&](int st, int buf) {
+        const int tb = t0 + 32 * st;
+        // V tile into LDS, row-major (columns past head_dim are never stored
+        // out), then the next step's V requested into the same registers
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+            *reinterpret_cast<u32x4 *>(vt + (RPI * v + vrow) * PITCH + 2 * vd) = vr[v];
+        if (st + 1 < nst) issue_v(st + 1);
+        // scores, transposed: lane -> row col, tokens 16 hf + 4 qd + i.  A
+        // step inside every row's range (and the split's) keeps all tokens
+        // and takes the path without per-token tests.
+        const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
+        u32x4 pb[RB];
+        int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
+        bool grow = false;
+        float alpha[RB];
+        auto softmax = [&](auto full_c) {
+            constexpr bool FULL = decltype(full_c)::value;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                f32x4_t sc[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < NCK; ++c)
+                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, kr[buf][hf][c]),
+                            __builtin_bit_cast(bf16x8_t, qb[rb][c]), x, 0, 0, 0);
+                    sc[hf] = x;
+                }
+                // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
+                int keep = 0xff;
+                if constexpr (!FULL) {
+                    keep = 0;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = tb + 16 * hf + 4 * qd + i;
+                            bool ok = t < t1 && t <= lim[rb];
+                            if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
+                            keep |= ok ? 1 << (4 * hf + i) : 0;
+                            sc[hf][i] = ok ? sc[hf][i] : -INFINITY;
+                        }
+                    }
+                    keep_any |= keep;
+                }
+                float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+                mx = max4(mx) * a.scale_log2;
+                // move the reference max only when the row's max passes it by
+                // more than the slack (a row with nothing kept so far keeps
+                // (m, l, o) = (-inf, 0, 0))
+                const bool mv = mx > m2[rb] + kRescaleSlack;
+                const float mn = mv ? mx : m2[rb];
+                alpha[rb] = mv ? exp2_fast(m2[rb] - mn) : 1.f;
+                grow |= mv;
+                m2[rb] = mn;
+                float p[8];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float e = exp2_fast(fmaf(sc[hf][i], a.scale_log2, -mn));
+                        p[4 * hf + i] = FULL || ((keep >> (4 * hf + i)) & 1) ? e : 0.f;
+                    }
+                }
+                pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                               pack_bf16(p[6], p[7])};
+                // l sums the weights as rounded for the product
+                float ps = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ps += bf_lo(pb[rb][e]) + bf_hi(pb[rb][e]);
+                lsum[rb] = fmaf(lsum[rb], alpha[rb], ps);
+            }
+        };
+        if (full) softmax(std::true_type{});
+        else softmax(std::false_type{});
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
+            }
+        }
+        // tokens no row keeps get V = 0 (with a mask they may hold anything)
+        uint32_t vkeep = 0xffffffffu;
+        if constexpr (MASK) {
+            keep_any = or16(keep_any);
+            if (__builtin_amdgcn_ballot_w64(keep_any != 0xff) != 0)
+                vkeep = 0;   // decided per element below
+        }
+        wave_lds_sync();
+        // P.V: A = V^T block n (tokens 4 qd .. +3 of each half, column 16 n + col)
+#pragma unroll
+        for (int n = 0; n < NDB; ++n) {
+            const unsigned char *base = vt + 2 * (16 * n + col);
+            uint32_t av[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r0 = (j < 2 ? 0 : 16) + 4 * qd + 2 * (j & 1);
+                uint32_t lo = *reinterpret_cast<const uint16_t *>(base + r0 * PITCH);
+                uint32_t hi = *reinterpret_cast<const uint16_t *>(base + (r0 + 1) * PITCH);
+                if constexpr (MASK) {
+                    if (vkeep == 0) {
+                        const int bit = 4 * (j >> 1) + 2 * (j & 1);
+                        lo = (keep_any >> bit) & 1 ? lo : 0u;
+                        hi = (keep_any >> (bit + 1)) & 1 ? hi : 0u;
+                    }
+                }
+                av[j] = lo | (hi << 16);
+            }
+            const u32x4 A = {av[0], av[1], av[2], av[3]};
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                                     __builtin_bit_cast(bf16x8_t, pb[rb]),
+                                                                     acc[rb][n], 0, 0, 0);
+        }
+        wave_lds_sync();
+    };
+
+    if (nst > 0) {
+        issue_k(0, 0);
+        issue_v(0);
+    }
+    for (int st = 0; st < nst; st += 2) {
+        if (st + 1 < nst) issue_k(st + 1, 1);
+        compute(st, 0);
+        if (st + 1 < nst) {
+            if (st + 2 < nst) issue_k(st + 2, 0);
+            compute(st + 1, 1);
+        }
+    }
+
+    // totals: lane l holds O[row col][16 n + 4 qd + i]
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float L = sum4(lsum[rb]);
+        if (rowid[rb] < 0) continue;
+        if (direct) {
+            uint16_t *op = a.out + rowid[rb] * a.D;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+            for (int n = 0; n < NDB; ++n) {
+                const int d = 16 * n + 4 * qd;
+                if (d >= a.D) continue;
+                const f32x4_t x = acc[rb][n];
+                *reinterpret_cast<u32x2 *>(op + d) =
+                    u32x2{pack_bf16(x[0] * inv, x[1] * inv), pack_bf16(x[2] * inv, x[3] * inv)};
+            }
+        } else {
+            const int64_t pi = rowid[rb] * a.nsplit + sp;
+            if (L > 0.f) {
+                float *po = a.part_o + pi * a.D;
+#pragma unroll
+                for (int n = 0; n < NDB; ++n) {
+                    const int d = 16 * n + 4 * qd;
+                    if (d < a.D) *reinterpret_cast<f32x4_t *>(po + d) = acc[rb][n];
+                }
+            }
+            if (qd == 0) {
+                a.part_ml[2 * pi] = m2[rb];
+                a.part_ml[2 * pi + 1] = L;
+            }
+        }
+    }
+}
+
+// One wave per output row (s, i, h) of a sequence with several splits:
+// log-sum-exp merge of its split partials (slots with l = 0 hold no token
+// and are skipped, their o never read) into the bf16 output.
+template <int DP>
+__global__ void __launch_bounds__(kPfThreads) prefill_merge_kernel(const PrefillArgs a) {
+    constexpr int E = DP / 64;   // elements per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kPfWaves + (threadIdx.x >> 6);
+    const int64_t nrows = (int64_t)a.S * a.Q * a.Hq;
+    if (row >= nrows) return;
+    const int s = (int)(row / ((int64_t)a.Q * a.Hq));
+    const int P = seq_tokens_pf(a, s);
+    const int nsp = P > 0 ? (P + a.span - 1) / a.span : 0;
+    if (nsp <= 1) return;
+    const float *ml = a.part_ml + row * a.nsplit * 2;
+    float M = -INFINITY;
+    for (int k = lane; k < nsp; k += 64)
+        if (ml[2 * k + 1] > 0.f) M = fmaxf(M, ml[2 * k]);
+    M = __builtin_amdgcn_readfirstlane(wave_max_f(M));
+    float o[E], L = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = 0.f;
+    const int d0 = lane * E;
+    for (int k = 0; k < nsp; ++k) {
+        const float lk = ml[2 * k + 1];
+        if (!(lk > 0.f)) continue;
+        const float wk = exp2_fast(ml[2 * k] - M);
+        L = fmaf(wk, lk, L);
+        if (d0 < a.D) {
+            const float *po = a.part_o + (row * a.nsplit + k) * a.D + d0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = fmaf(wk, po[e], o[e]);
+        }
+    }
+    if (d0 < a.D) {
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        uint16_t *op = a.out + row * a.D + d0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) op[e] = f32_to_bf16(o[e] * inv);
+    }
+}
+
+template <int DP, int RB, bool MASK, bool P16>
+hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, const AttendEvents &ev) {
+    const int64_t nitems = (int64_t)a.S * a.nsplit * a.Hkv * a.ntiles;
+    int64_t nwg = (nitems + kPfWaves - 1) / kPfWaves;
+    nwg = (nwg + 7) / 8 * 8;
+    if (ev.before) {
+        hipError_t e = hipEventRecord(ev.before, st);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((prefill_kernel<DP, RB, MASK, P16>), dim3((unsigned)nwg), dim3(kPfThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev.after) {
+        e = hipEventRecord(ev.after, st);
+        if (e != hipSuccess) return e;
+    }
+    if (a.nsplit > 1) {
+        const int64_t rows = (int64_t)a.S * a.Q * a.Hq;
+        hipLaunchKernelGGL((prefill_merge_kernel<DP>), dim3((unsigned)((rows + kPfWaves - 1) / kPfWaves)),
+                           dim3(kPfThreads), 0, st, a);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+// Instantiated shapes: head dims up to 128 take 1, 2 or 4 row blocks per wave
+// (4 only without a mask at 128: with one it would spill), 256 takes one.
+int prefill_max_rb(int dp, bool mask) {
+    if (dp == 256) return 1;
+    if (dp == 128 && mask) return 2;
+    return 4;
+}
+
+template <int DP, int RB, bool MASK>
+hipError_t launch_prefill_p(const PrefillArgs &a, hipStream_t st, const AttendEvents &ev) {
+    return a.bs % 16 == 0 ? launch_prefill_t<DP, RB, MASK, true>(a, st, ev)
+                          : launch_prefill_t<DP, RB, MASK, false>(a, st, ev);
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, int dp, int rb, hipStream_t st, const AttendEvents &ev) {
+    const bool m = a.mask != nullptr;
+    switch (dp) {
+        case 64:
+            if (rb == 1) return m ? launch_prefill_p<64, 1, true>(a, st, ev) : launch_prefill_p<64, 1, false>(a, st, ev);
+            if (rb == 2) return m ? launch_prefill_p<64, 2, true>(a, st, ev) : launch_prefill_p<64, 2, false>(a, st, ev);
+            return m ? launch_prefill_p<64, 4, true>(a, st, ev) : launch_prefill_p<64, 4, false>(a, st, ev);
+        case 128:
+            if (rb == 1) return m ? launch_prefill_p<128, 1, true>(a, st, ev) : launch_prefill_p<128, 1, false>(a, st, ev);
+            if (rb == 2 || m) return m ? launch_prefill_p<128, 2, true>(a, st, ev) : launch_prefill_p<128, 2, false>(a, st, ev);
+            return launch_prefill_p<128, 4, false>(a, st, ev);
+        default:
+            return m ? launch_prefill_p<256, 1, true>(a, st, ev) : launch_prefill_p<256, 1, false>(a, st, ev);
+    }
+}
+
+}  // namespace pda

@@ -259,3 +259,70 @@ def test_attn_paged_decode_rejects_host_tensors():
         pda.attn_paged_decode(q, kc, kc, bt, lens)
     with pytest.raises(ValueError):
         pda.attn_paged_decode(q[:, 0], kc, kc, bt, lens)
+
+
+def test_prefill_workspace_sizes():
+    """Split partials of max_seqs * q_len * Hq rows, ceil(cap / bps) slots each,
+    (head_dim + 2) floats per slot plus 16 bytes of alignment padding; none
+    when one split covers the page list."""
+    d = dims()   # 4 seqs, 8 q heads, head_dim 64, block_size 16, capacity 32
+    for q_len in (1, 7):
+        rows = 4 * q_len * 8
+        for bps in (1, 3, 16):
+            slots = -(-32 // bps)
+            assert pda.pda_prefill_workspace_bytes(d, q_len, bps) == rows * slots * 66 * 4 + 16
+        assert pda.pda_prefill_workspace_bytes(d, q_len, 32) == 0
+        assert pda.pda_prefill_workspace_bytes(d, q_len, 99) == 0
+        # the library's choice never splits below 256 tokens (16 pages here)
+        assert pda.pda_prefill_workspace_bytes(d, q_len, 0) == rows * 2 * 66 * 4 + 16
+    assert pda.pda_prefill_workspace_bytes(d, 0, 0) == 0
+    assert pda.pda_prefill_workspace_bytes(dims(num_q_heads=6, num_kv_heads=4), 4, 0) == 0
+
+
+def test_prefill_validation_before_enqueue():
+    """pda_prefill checks every argument before anything is enqueued
+    (addresses are never dereferenced)."""
+    d = dims()
+    st = (16 * 2 * 64, 2 * 64, 64)
+    args = dict(dims=d, q_len=5, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_tables=FAKE,
+                block_counts=FAKE, last_block_valid=None, last_block_valid_default=16,
+                num_seqs=4, strides=st, causal=True, kv_mask=None, mask_seq_stride=0,
+                mask_q_stride=0, workspace=FAKE, out=FAKE, blocks_per_split=0,
+                rows_per_wave=0, stream=0, workspace_bytes=pda.pda_prefill_workspace_bytes(d, 5))
+    cases = [
+        (dict(q=None), pda.PDA_ERR_NULL),
+        (dict(out=None), pda.PDA_ERR_NULL),
+        (dict(block_tables=None), pda.PDA_ERR_NULL),
+        (dict(q=FAKE + 2), pda.PDA_ERR_ALIGN),
+        (dict(out=FAKE + 8), pda.PDA_ERR_ALIGN),
+        (dict(workspace=FAKE + 4), pda.PDA_ERR_ALIGN),
+        (dict(strides=(st[0], st[1] + 4, st[2])), pda.PDA_ERR_ALIGN),
+        (dict(q_len=0), pda.PDA_ERR_DIMS),
+        (dict(q_len=1 << 23), pda.PDA_ERR_DIMS),
+        (dict(rows_per_wave=48), pda.PDA_ERR_DIMS),
+        (dict(blocks_per_split=-2), pda.PDA_ERR_DIMS),
+        (dict(kv_mask=FAKE, mask_seq_stride=-1), pda.PDA_ERR_DIMS),
+        (dict(kv_mask=FAKE, mask_q_stride=-3), pda.PDA_ERR_DIMS),
+        (dict(num_seqs=5), pda.PDA_ERR_MAX_SEQS),
+        (dict(workspace_bytes=16), pda.PDA_ERR_WORKSPACE),
+        (dict(workspace=None, workspace_bytes=0), pda.PDA_ERR_WORKSPACE),
+        (dict(dims=dims(num_q_heads=6, num_kv_heads=4)), pda.PDA_ERR_GQA),
+        (dict(dims=dims(head_dim=260)), pda.PDA_ERR_HEAD_DIM),
+    ]
+    for change, status in cases:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_prefill(**{**args, **change})
+        assert e.value.status == status, (change, e.value)
+    pda.pda_prefill(**{**args, "num_seqs": 0})
+
+
+def test_attn_paged_prefill_rejects_host_tensors():
+    import torch
+    q = torch.zeros(2, 3, 4, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(8, 1, 2, 64, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    lens = torch.tensor([3, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pda.attn_paged_prefill(q, kc, kc, bt, lens)
+    with pytest.raises(ValueError):
+        pda.attn_paged_prefill(q[:, 0], kc, kc, bt, lens)
