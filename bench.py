@@ -1,4 +1,4 @@
-"""Benchmark: paged GQA decode attention on one MI355X.
+"""Benchmark: paged GQA decode (and prefill) attention on one MI355X.
 
 One step is one pda_decode call (split-KV attention kernel + log-sum-exp merge
 kernel) over the ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
@@ -10,6 +10,10 @@ one JSON line: `value` from the timed steps; `roofline.achieved` from the
 attention kernel's own average duration, taken with an event pair around each
 of its launches in a second pass over the same steps; `roofline.traffic` from
 the committed counter summary when the kernel sources still match it.
+
+A prefill workload ("prefill-2048", "prefill-chunk-b16") times one
+pda_prefill call per step instead and reports TFLOP/s against the bf16 MFMA
+peak (the kernel is bound by the matrix cores, not by HBM).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--blocks-per-split N] [--no-cpu-baseline] [--no-kernel-events]
@@ -27,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+PEAK_MFMA_BF16_TFS = 2500.0   # MI355X dense bf16 matrix peak, TFLOP/s
 
 
 def parse():
@@ -35,7 +40,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="ragged-b64",
-                    choices=["tiny", "llama3-8b-b16", "ragged-b64", "wide-head-d256", "scratch-b256"])
+                    choices=["tiny", "llama3-8b-b16", "ragged-b64", "wide-head-d256", "scratch-b256",
+                             "prefill-2048", "prefill-chunk-b16"])
+    ap.add_argument("--rows-per-wave", type=int, default=0, help="prefill: query rows per wave")
     ap.add_argument("--blocks-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -73,30 +80,61 @@ def cpu_baseline(w, min_seconds):
                       f"{reps} repetition(s), fp64 C oracle with OpenMP"}
 
 
-def kernel_sources_sha256():
-    """Hash of the HIP sources that decide the attention kernel and its launch."""
+# The sources each kernel's code and launch come from (a committed counter
+# summary holds for the kernel only while these hash to its recorded value).
+KERNEL_SOURCES = {
+    "attend_kernel": ["pda_device.h", "pda_internal.h", "pda_kernels.hip"],
+    "prefill_kernel": ["pda_device.h", "pda_internal.h", "pda_prefill.hip"],
+}
+
+
+def kernel_sources_sha256(kernel="attend_kernel"):
+    """Hash of the HIP sources that decide the kernel and its launch."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_gqa_decode_pda_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def committed_traffic(workload_name):
+def cpu_baseline_prefill(w, min_seconds, sample_rows=4096):
+    """The fp64 oracle as it stands, on the host cores, over a seeded sample of
+    the workload's (sequence, query, q head) rows (repeated until
+    `min_seconds` have passed), as TFLOP/s of the sampled rows' own flops."""
+    import oracle
+    threads = oracle.host_threads()
+    S, Q, Hq, D = w.qc.shape
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = np.sort(rng.choice(S * Q * Hq, size=min(sample_rows, S * Q * Hq), replace=False))
+    keys = w.prefill_keys(True).reshape(-1)[rows // Hq]
+    flops = int(keys.sum()) * 4 * D
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill_workload(w, rows=rows, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    per = el / reps
+    return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows.size} seeded (sequence, query, q head) rows of {S * Q * Hq}, "
+                      f"{reps} repetition(s), fp64 C oracle with OpenMP"}
+
+
+def committed_traffic(workload_name, kernel="attend_kernel"):
     """HBM bytes per attention launch from the committed counter summary for
     this workload, or None when it is missing or the kernel sources changed
     since the counters were taken."""
     import re
-    path = os.path.join(ROOT, "profiles", f"attend_kernel_{workload_name}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_name}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not sha or not val or sha.group(1) != kernel_sources_sha256():
+    if not sha or not val or sha.group(1) != kernel_sources_sha256(kernel):
         return None
     return int(val.group(1))
 
@@ -132,6 +170,9 @@ def main():
     w = workloads.named(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if w.is_prefill:
+        main_prefill(args, w, torch, pda, dev)
+        return
     b, c, v = w.stacked_tiles()
     T = len(w.tiles)
     dims = pda.pda_dims(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
@@ -275,6 +316,87 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def main_prefill(args, w, torch, pda, dev):
+    """One step = one causal pda_prefill call over the workload's chunks."""
+    b, c, v = w.stacked_tiles()
+    S, Q, Hq, D = w.qc.shape
+    dims = pda.pda_dims(S, Hq, w.num_kv_heads, D, w.block_size, w.tile_capacity)
+    qc = torch.from_numpy(w.qc.view(np.int16)).to(dev)
+    pool = torch.from_numpy(w.pool.view(np.int16)).to(dev)
+    table, count, lastv = (torch.from_numpy(x[0]).to(dev) for x in (b, c, v))
+    bps, rpw = args.blocks_per_split, args.rows_per_wave
+    nb = pda.pda_prefill_workspace_bytes(dims, Q, bps)
+    ws = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=dev) if nb else None
+    out = torch.empty(S, Q, Hq, D, dtype=torch.int16, device=dev)
+    kp, vp = pool.data_ptr() + 2 * w.k_base, pool.data_ptr() + 2 * w.v_base
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pda.pda_prefill(dims, Q, qc, kp, vp, table, count, lastv, w.block_size, S, w.strides,
+                        True, None, 0, 0, ws, out, bps, rpw, stream, workspace_bytes=nb)
+
+    n_ev = 0 if args.no_kernel_events else args.steps
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in ev_b + ev_a:
+        e.record(stream)
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kernel_us = None
+    if n_ev:
+        log(f"timing {args.steps} steps with per-launch attention-kernel events")
+        for i in range(n_ev):
+            pda.pda_debug_time_attention(ev_b[i], ev_a[i])
+            step()
+        torch.cuda.synchronize()
+        kernel_us = sum(x.elapsed_time(y) for x, y in zip(ev_b, ev_a)) * 1e3 / n_ev
+    flops = w.prefill_flops(True)
+    tfs = flops / (ms * 1e-3) / 1e12
+    achieved = flops / ((kernel_us if kernel_us else ms * 1e3) * 1e-6) / 1e12
+    res = {
+        "metric": "paged GQA prefill attention achieved TFLOP/s (causal q.K^T and P.V flops / time)",
+        "value": round(tfs, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_call": round(ms * 1e3, 2),
+        "pct_of_peak": round(100 * tfs / PEAK_MFMA_BF16_TFS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": S, "q_len": Q, "num_q_heads": Hq,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": D, "block_size": w.block_size,
+                   "total_tokens": w.total_tokens, "causal": True, "algorithmic_flops": flops,
+                   "algorithmic_bytes": w.prefill_bytes(), "layout": w.layout, "api": "pda_prefill",
+                   "blocks_per_split": bps, "rows_per_wave": rpw, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma",
+                     "kernel": "prefill_kernel (paged MFMA chunk attention), average over the timed "
+                               "launches" if kernel_us else "pda_prefill step (all launches)",
+                     "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_MFMA_BF16_TFS, 4),
+                     "traffic": committed_traffic(w.name, "prefill_kernel") if kernel_us else None,
+                     "algorithmic_flops_per_launch": flops,
+                     "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
+                     "launches_per_step": 1},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle, sampled rows)")
+        res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

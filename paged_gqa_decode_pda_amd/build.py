@@ -25,6 +25,12 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
+# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
+# VGPRs (the compiler's default form there moves every accumulator between
+# AGPRs and VGPRs on each step).
+EXTRA_FLAGS = {"pda_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
         if cand and (os.path.sep not in cand or os.path.exists(cand)):
@@ -37,7 +43,7 @@ def build(verbose: bool = False, extra=()) -> str:
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(HERE, "csrc", os.path.basename(src) + ".o")
-        cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", "-o", obj, src]
+        cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), *extra, "-c", "-o", obj, src]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append(subprocess.Popen(cmd))
