@@ -25,10 +25,11 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
-# Per-source extra flags.  The prefill kernel keeps its MFMA accumulators in
-# VGPRs (the compiler's default form there moves every accumulator between
-# AGPRs and VGPRs on each step).
-EXTRA_FLAGS = {"pda_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source extra flags (none at present).  Forcing the prefill kernel's
+# MFMA results into VGPRs (-amdgpu-mfma-vgpr-form=1) removes the
+# accumulator copies between AGPRs and VGPRs but measured slower at 64 rows
+# per wave, the default shape.
+EXTRA_FLAGS = {}
 
 
 def hipcc() -> str:
