@@ -9,7 +9,8 @@ the GPU library.
 each gathered token list, binary64 throughout); ``prefill`` is the same
 definition for a chunk of queries per sequence, each keeping the keys up to
 its own position when causal (AstrAI "CUDA Kernels", "Python Wrappers":
-is_causal and the [batch, q_len, kv_len] mask); ``merge`` is the log-sum-exp
+is_causal and the [batch, q_len, kv_len] mask); ``rope`` is rotary embedding
+in its complex-multiply form; ``merge`` is the log-sum-exp
 fold of two (m, l, o) running states.  The operation follows the AstrAI
 "CUDA Kernels" page (section "Python Wrappers": blhd layout, scale
 1/sqrt(head_dim)) and the spark_storage "tiled_attention.rs" page (header
@@ -58,6 +59,8 @@ def load_library(path):
                                        i64, i64, i32, P, P, P, i32, P, i64, i64, P, i64, P, P,
                                        P, P, ctypes.c_int]
     lib.pda_oracle_prefill.restype = ctypes.c_int
+    lib.pda_oracle_rope.argtypes = [i64, i32, i32, P, P, P, i32, P, P]
+    lib.pda_oracle_rope.restype = ctypes.c_int
     return lib
 
 
@@ -227,6 +230,43 @@ def prefill_workload(w, causal=True, mask=None, rows=None, threads=None):
     b, c, v = w.stacked_tiles()
     return prefill(w.qc, w.pool, w.k_base, w.v_base, w.strides, w.num_kv_heads, w.block_size,
                    b[0], c[0], v[0], causal=causal, mask=mask, rows=rows, threads=threads)
+
+
+def rope(x, cos_table, sin_table, positions, lib=None):
+    """Rotary embedding in its complex-multiply form (AstrAI "CUDA Kernels",
+    "Rotary Embedding Kernel" / "Rotary Backend"): consecutive element pairs
+    (x[2j], x[2j+1]) of each row times cos + i sin of the token's position.
+
+    x           uint16 bf16 bits [T, H, D] (any leading shape flattening to T
+                tokens: [B, L, H, D] is read as T = B * L)
+    cos_table, sin_table   float32 [max_positions, D / 2]
+    positions   int32 [T] (same leading shape as x), clamped to the table
+
+    Returns the unrounded float64 result with x's shape.
+    """
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    shape = x.shape
+    H, D = shape[-2], shape[-1]
+    T = int(np.prod(shape[:-2]))
+    ct = np.ascontiguousarray(cos_table, dtype=np.float32)
+    st = np.ascontiguousarray(sin_table, dtype=np.float32)
+    assert ct.shape == st.shape and ct.ndim == 2 and ct.shape[1] * 2 == D
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32).reshape(-1))
+    assert pos.size == T
+    out = np.empty(shape, np.float64)
+    rc = (lib or _load()).pda_oracle_rope(T, H, D, x.ctypes.data, ct.ctypes.data, st.ctypes.data,
+                                          ct.shape[0], pos.ctypes.data, out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its inputs (code {rc})")
+    return out
+
+
+def rope_tables(max_positions, head_dim, base=10000.0):
+    """fp32 cos/sin tables of the usual frequencies: angle of pair j at position
+    p = p * base^(-2j / head_dim), evaluated in float64 and rounded once."""
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    ang = np.arange(max_positions, dtype=np.float64)[:, None] * base ** (-2.0 * j / head_dim)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def merge(a, b):

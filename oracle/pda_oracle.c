@@ -32,6 +32,9 @@
  *  - same page, "Overview" table and section "Attention Backend": prefill
  *    attention (a chunk of q_len > 1 query tokens per sequence) next to
  *    decode, dispatched by q_len.
+ *  - same page, "Rotary Embedding Kernel" and "Rotary Backend": rotary
+ *    embedding from fp32 cos/sin tables, defined by its complex-multiply
+ *    form (consecutive element pairs as complex numbers times cos + i sin).
  *
  * Readings where the pages are silent:
  *  - q head h reads kv head g = h / G (contiguous groups of G q heads).
@@ -297,4 +300,43 @@ int pda_oracle_prefill(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int
         free(score);
     }
     return status;
+}
+
+/*
+ * Rotary embedding, the complex-multiply form: element pair j of a row,
+ * (x[2j], x[2j+1]), read as the complex number x[2j] + i x[2j+1], times
+ * cos + i sin of the token's position:
+ *
+ *   out[2j]     = x[2j] cos_j - x[2j+1] sin_j
+ *   out[2j + 1] = x[2j] sin_j + x[2j+1] cos_j
+ *
+ * with cos_j = cos_table[p * (head_dim / 2) + j] (fp32, widened exactly) and
+ * p = positions[token], clamped to [0, max_positions - 1].
+ *
+ *   x          bf16 [num_tokens, num_heads, head_dim]
+ *   out        fp64 [num_tokens, num_heads, head_dim] (unrounded)
+ *
+ * Returns 0, or -2 on bad dimensions (odd head_dim, non-positive sizes).
+ */
+int pda_oracle_rope(int64_t num_tokens, int32_t num_heads, int32_t head_dim, const uint16_t *x,
+                    const float *cos_table, const float *sin_table, int32_t max_positions,
+                    const int32_t *positions, double *out) {
+    if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || head_dim % 2 != 0 || max_positions <= 0)
+        return -2;
+    const int32_t half = head_dim / 2;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int32_t p = clamp_i32(positions[t], 0, max_positions - 1);
+        const float *c = cos_table + (int64_t)p * half;
+        const float *sn = sin_table + (int64_t)p * half;
+        for (int32_t h = 0; h < num_heads; ++h) {
+            const int64_t row = (t * num_heads + h) * head_dim;
+            for (int32_t j = 0; j < half; ++j) {
+                const double re = bf16_to_f64(x[row + 2 * j]), im = bf16_to_f64(x[row + 2 * j + 1]);
+                const double cj = (double)c[j], sj = (double)sn[j];
+                out[row + 2 * j] = re * cj - im * sj;
+                out[row + 2 * j + 1] = re * sj + im * cj;
+            }
+        }
+    }
+    return 0;
 }

@@ -443,3 +443,92 @@ def pin_prefill_mask_library(prefill, attend=None):
 PREFILL_PINS = [pin_prefill_square_library_causal, pin_prefill_causal_is_tril,
                 pin_prefill_future_keys, pin_prefill_noncausal_is_decode,
                 pin_prefill_mask_library]
+
+
+# ---------------------------------------------------------------------------
+# Rotary embedding.  Each pin takes a ``rope`` callable with the signature of
+# ``oracle.rope``.
+
+def workloads_bits_to_f32(x):
+    from workloads import bf16_bits_to_f32
+    return bf16_bits_to_f32(x)
+
+
+def _rope_case(rng, shape, max_pos=50):
+    x = to_bits(rng.standard_normal(shape))
+    pos = rng.integers(0, max_pos, size=shape[:-2]).astype(np.int32)
+    return x, pos
+
+
+def pin_rope_complex_library(rope):
+    """Equals torch's float64 complex multiply (view_as_complex over
+    consecutive pairs, times cos + i sin of the position: the pages' own
+    fallback definition) for [B, L, H, D] and [T, H, D] inputs."""
+    import torch
+    from oracle import rope_tables
+    rng = np.random.Generator(np.random.PCG64(51))
+    for shape in ((2, 3, 4, 16), (7, 2, 64), (1, 1, 1, 2)):
+        D = shape[-1]
+        ct, st = rope_tables(50, D)
+        x, pos = _rope_case(rng, shape)
+        got = rope(x, ct, st, pos)
+        xf = torch.from_numpy(workloads_bits_to_f32(x).astype(np.float64).reshape(*shape[:-1], D // 2, 2))
+        z = torch.view_as_complex(xf.contiguous())
+        f = torch.complex(torch.from_numpy(ct[pos].astype(np.float64)),
+                          torch.from_numpy(st[pos].astype(np.float64))).unsqueeze(-2)
+        want = torch.view_as_real(z * f).reshape(shape).numpy()
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def pin_rope_identity_and_quarter_turn(rope):
+    """cos = 1, sin = 0 leaves x unchanged bit for bit; cos = 0, sin = 1 (a
+    quarter turn) maps each pair (a, b) to (-b, a) exactly."""
+    rng = np.random.Generator(np.random.PCG64(52))
+    x, pos = _rope_case(rng, (4, 3, 32), max_pos=5)
+    xf = workloads_bits_to_f32(x).astype(np.float64)
+    one, zero = np.ones((5, 16), np.float32), np.zeros((5, 16), np.float32)
+    np.testing.assert_array_equal(rope(x, one, zero, pos), xf)
+    q = rope(x, zero, one, pos)
+    np.testing.assert_array_equal(q[..., 0::2], -xf[..., 1::2])
+    np.testing.assert_array_equal(q[..., 1::2], xf[..., 0::2])
+
+
+def pin_rope_positions(rope):
+    """Each token takes the table row of its own position (positions outside
+    the table clamp to its first or last row): a table whose row p rotates by
+    a distinct angle per row reproduces, token by token, the rotation by
+    that row's angle."""
+    rng = np.random.Generator(np.random.PCG64(53))
+    T, H, D, P = 9, 2, 8, 6
+    ang = rng.uniform(-3, 3, size=(P, D // 2))
+    ct, st = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    x = to_bits(rng.standard_normal((T, H, D)))
+    pos = np.array([0, 5, 3, 3, -2, 7, 1, 4, 2], np.int32)
+    got = rope(x, ct, st, pos)
+    xf = workloads_bits_to_f32(x).astype(np.float64)
+    for t in range(T):
+        p = min(max(int(pos[t]), 0), P - 1)
+        c, s = ct[p].astype(np.float64), st[p].astype(np.float64)
+        for h in range(H):
+            a, b = xf[t, h, 0::2], xf[t, h, 1::2]
+            np.testing.assert_array_equal(got[t, h, 0::2], a * c - b * s)
+            np.testing.assert_array_equal(got[t, h, 1::2], a * s + b * c)
+
+
+def pin_rope_norm(rope):
+    """A rotation keeps each pair's length: |out pair|^2 = |x pair|^2 (c^2 + s^2)
+    for the fp32 table values (invariant)."""
+    from oracle import rope_tables
+    rng = np.random.Generator(np.random.PCG64(54))
+    ct, st = rope_tables(64, 128)
+    x, pos = _rope_case(rng, (5, 4, 128), max_pos=64)
+    got = rope(x, ct, st, pos)
+    xf = workloads_bits_to_f32(x).astype(np.float64)
+    n_in = (xf[..., 0::2] ** 2 + xf[..., 1::2] ** 2) * \
+        (ct[pos].astype(np.float64) ** 2 + st[pos].astype(np.float64) ** 2)[:, None, :]
+    n_out = got[..., 0::2] ** 2 + got[..., 1::2] ** 2
+    np.testing.assert_allclose(n_out, n_in, rtol=1e-12, atol=1e-14)
+
+
+ROPE_PINS = [pin_rope_complex_library, pin_rope_identity_and_quarter_turn, pin_rope_positions,
+             pin_rope_norm]

@@ -39,6 +39,12 @@ MUTANTS = {
                          "q + (((int64_t)s * num_q_heads + h) * q_len + i) * head_dim"),
     "prefill_mask_query_shared": ("(int64_t)i * mask_q_stride", "(int64_t)0 * mask_q_stride"),
     "prefill_mask_seq_shared": ("mask + (int64_t)s * mask_seq_stride", "mask + (int64_t)0 * mask_seq_stride"),
+    "rope_sin_sign": ("out[row + 2 * j] = re * cj - im * sj;", "out[row + 2 * j] = re * cj + im * sj;"),
+    "rope_half_split": ("re = bf16_to_f64(x[row + 2 * j]), im = bf16_to_f64(x[row + 2 * j + 1]);",
+                        "re = bf16_to_f64(x[row + j]), im = bf16_to_f64(x[row + j + half]);"),
+    "rope_cos_sin_swapped": ("cj = (double)c[j], sj = (double)sn[j];", "cj = (double)sn[j], sj = (double)c[j];"),
+    "rope_position_ignored": ("clamp_i32(positions[t], 0, max_positions - 1)",
+                              "clamp_i32((int32_t)(t % max_positions), 0, max_positions - 1)"),
 }
 
 
@@ -60,6 +66,9 @@ def test_mutant_fails_a_pin(name, tmp_path):
     def prefill(**kw):
         return oracle.prefill(**kw, lib=lib)
 
+    def rope(*a, **kw):
+        return oracle.rope(*a, **kw, lib=lib)
+
     failed = []
     for pin in oracle_pins.ALL_PINS:
         try:
@@ -73,6 +82,11 @@ def test_mutant_fails_a_pin(name, tmp_path):
     for pin in oracle_pins.PREFILL_PINS:
         try:
             pin(prefill, attend)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    for pin in oracle_pins.ROPE_PINS:
+        try:
+            pin(rope)
         except (AssertionError, ValueError, FloatingPointError):
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"

@@ -31,6 +31,11 @@ def test_prefill_rows_subset_matches_full():
         np.testing.assert_array_equal(part[key], full[key].reshape(-1, 8)[rows])
 
 
+@pytest.mark.parametrize("pin", oracle_pins.ROPE_PINS, ids=lambda f: f.__name__)
+def test_rope_pin(pin):
+    pin(oracle.rope)
+
+
 def test_tiled_merge_pin():
     oracle_pins.pin_tiled_merge(oracle.attend, oracle.merge)
 
