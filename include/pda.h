@@ -20,7 +20,10 @@
  *        "Attention Backend" (decode through the paged kernel with page
  *        size 1) and the "Overview" table (GQA decode with split-KV; paged
  *        KV-cache decode; GQA prefill), the is_causal switch and the
- *        [batch, q_len, kv_len] mask of "Python Wrappers" for prefill.
+ *        [batch, q_len, kv_len] mask of "Python Wrappers" for prefill;
+ *        "Rotary Embedding Kernel" and "Rotary Backend" (fused cos/sin
+ *        lookup and rotation, fp32 tables, bf16 rows; its complex-multiply
+ *        form defines the pairing).
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
@@ -252,6 +255,46 @@ pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const
                        int32_t causal, const uint8_t *kv_mask, int64_t mask_seq_stride,
                        int64_t mask_q_stride, void *workspace, size_t workspace_bytes, void *out,
                        int32_t blocks_per_split, int32_t rows_per_wave, void *stream);
+
+/* Rotary embedding ([CK] Rotary Embedding Kernel, Rotary Backend): element
+ * pair j of each row, (x[2j], x[2j+1]), read as a complex number, times
+ * cos + i sin of the token's position:
+ *   out[2j] = x[2j] cos_j - x[2j+1] sin_j,  out[2j+1] = x[2j] sin_j + x[2j+1] cos_j
+ * computed in fp32 and rounded once to bf16 (nearest even).
+ *   x, out        device bf16 [num_tokens, num_heads, head_dim] (blhd rows with
+ *                 batch and seq_len flattened); out may equal x (in place)
+ *   cos_table, sin_table  device fp32 [max_positions, head_dim / 2]
+ *   positions     device int32 [num_tokens]: each token's position, clamped to
+ *                 [0, max_positions - 1] on the device
+ * head_dim a multiple of 8 in [8, 256] (PDA_ERR_HEAD_DIM); x, out and the
+ * tables 16-byte aligned, positions 4-byte aligned (PDA_ERR_ALIGN). */
+pda_status pda_rope(const void *x, void *out, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, const float *cos_table, const float *sin_table,
+                    int32_t max_positions, const int32_t *positions, void *stream);
+
+/* Rotary embedding fused with the paged-cache write of new tokens: token t's
+ * K row is rotated as pda_rope does and stored, with its V row unchanged, at
+ * slot positions[t] % block_size of page
+ * block_tables[token_seq[t] * tile_capacity + positions[t] / block_size] of
+ * the pools addressed with `strides` (the layouts of pda_decode).
+ *   dims          num_kv_heads, head_dim, block_size, tile_capacity of the cache;
+ *                 max_seqs bounds token_seq
+ *   k_new, v_new  device bf16 [num_tokens, num_kv_heads, head_dim]
+ *   token_seq     device int32 [num_tokens]: the sequence each token belongs to
+ *   positions     device int32 [num_tokens]: its position in that sequence
+ *   block_tables  device int32 [max_seqs, tile_capacity]
+ *   k_pool, v_pool  device bf16 pools, written
+ * A token whose sequence is outside [0, max_seqs), whose position is
+ * negative or whose page index reaches tile_capacity is not written; the
+ * cos/sin row is the position clamped to the table.  Device-side contract:
+ * the page ids used address pages inside the pools, and no two tokens of a
+ * call share a slot. */
+pda_status pda_rope_append_kv(const pda_dims *dims, const void *k_new, const void *v_new,
+                              int64_t num_tokens, const int32_t *token_seq,
+                              const int32_t *positions, const float *cos_table,
+                              const float *sin_table, int32_t max_positions,
+                              const int32_t *block_tables, void *k_pool, void *v_pool,
+                              pda_strides strides, void *stream);
 
 /* Timing diagnostics, for benchmarks that need the attention kernel's own
  * duration: arms the calling thread's next pda_decode, pda_decode_masked,

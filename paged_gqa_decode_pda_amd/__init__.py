@@ -42,7 +42,8 @@ EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_bl
             "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
             "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
             "pda_step_tile", "pda_finalize", "pda_decode", "pda_decode_masked",
-            "pda_prefill_workspace_bytes", "pda_prefill", "pda_debug_time_attention",
+            "pda_prefill_workspace_bytes", "pda_prefill", "pda_rope", "pda_rope_append_kv",
+            "pda_debug_time_attention",
             "pda_status_string", "pda_last_error"]
 
 
@@ -98,6 +99,9 @@ _sig("pda_decode_masked", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32,
 _sig("pda_prefill_workspace_bytes", _sz, _PD, _i32, _i32)
 _sig("pda_prefill", ctypes.c_int, _PD, _i32, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _i32,
      _P, _i64, _i64, _P, _sz, _P, _i32, _i32, _P)
+_sig("pda_rope", ctypes.c_int, _P, _P, _i64, _i32, _i32, _P, _P, _i32, _P, _P)
+_sig("pda_rope_append_kv", ctypes.c_int, _PD, _P, _P, _i64, _P, _P, _P, _P, _i32, _P, _P, _P,
+     pda_strides, _P)
 _sig("pda_debug_time_attention", ctypes.c_int, _P, _P)
 _sig("pda_status_string", ctypes.c_char_p, ctypes.c_int)
 _sig("pda_last_error", ctypes.c_char_p)
@@ -284,6 +288,47 @@ def pda_prefill(dims, q_len: int, q, k_pool, v_pool, block_tables, block_counts,
                             1 if causal else 0, _addr(kv_mask), int(mask_seq_stride),
                             int(mask_q_stride), _addr(workspace), nb, _addr(out),
                             blocks_per_split, rows_per_wave, _stream(stream)))
+
+
+def pda_rope(x, out, num_tokens: int, num_heads: int, head_dim: int, cos_table, sin_table,
+             max_positions: int, positions, stream=None) -> None:
+    _check(_lib.pda_rope(_addr(x), _addr(out), int(num_tokens), num_heads, head_dim,
+                         _addr(cos_table), _addr(sin_table), int(max_positions), _addr(positions),
+                         _stream(stream)))
+
+
+def pda_rope_append_kv(dims, k_new, v_new, num_tokens: int, token_seq, positions, cos_table,
+                       sin_table, max_positions: int, block_tables, k_pool, v_pool, strides,
+                       stream=None) -> None:
+    d = _dims(dims)
+    _check(_lib.pda_rope_append_kv(ctypes.byref(d), _addr(k_new), _addr(v_new), int(num_tokens),
+                                   _addr(token_seq), _addr(positions), _addr(cos_table),
+                                   _addr(sin_table), int(max_positions), _addr(block_tables),
+                                   _addr(k_pool), _addr(v_pool), _strides(strides),
+                                   _stream(stream)))
+
+
+def apply_rotary_emb(x, freqs_cis, positions, out=None, stream=None):
+    """Rotary embedding in the pages' calling convention: x [batch, seq_len,
+    n_heads, head_dim] bf16 (blhd), freqs_cis = (cos, sin) fp32 tables
+    [max_positions, head_dim / 2], positions int32 [batch, seq_len] (each
+    token's position).  Returns out (a new tensor unless given; out=x rotates
+    in place).  Argument marshalling only; the rotation runs in the library."""
+    import torch
+    cos_t, sin_t = freqs_cis
+    if x.dim() != 4 or x.dtype != torch.bfloat16 or not x.is_contiguous() or x.device.type != "cuda":
+        raise ValueError("x must be a contiguous bfloat16 device tensor [batch, seq_len, n_heads, head_dim]")
+    B, L, H, D = x.shape
+    for t in (cos_t, sin_t):
+        if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] * 2 != D or t.device.type != "cuda":
+            raise ValueError("cos and sin must be float32 device tensors [max_positions, head_dim / 2]")
+    pos = positions.to(device=x.device, dtype=torch.int32).contiguous()
+    if pos.numel() != B * L:
+        raise ValueError("positions must hold one entry per token")
+    if out is None:
+        out = torch.empty_like(x)
+    pda_rope(x, out, B * L, H, D, cos_t.contiguous(), sin_t.contiguous(), cos_t.shape[0], pos, stream)
+    return out
 
 
 def _paged_args(q, k_cache, v_cache, block_table, seq_lens):

@@ -13,6 +13,7 @@
 #include <new>
 
 #include "pda_internal.h"
+#include "pda_rope.h"
 
 struct pda_plan {
     pda_dims dims;
@@ -523,6 +524,95 @@ pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
     hipError_t e = pda::launch_prefill(a, dp, rb, static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "prefill launch");
+}
+
+namespace {
+
+pda_status check_rope_common(const void *x, const float *cos_table, const float *sin_table,
+                             const int32_t *positions, int64_t num_tokens, int32_t num_heads,
+                             int32_t head_dim, int32_t max_positions) {
+    if (!x || !cos_table || !sin_table || !positions)
+        return fail(PDA_ERR_NULL, "a required pointer is NULL");
+    if (num_tokens < 0 || num_heads < 1 || max_positions < 1)
+        return fail(PDA_ERR_DIMS, "num_tokens >= 0, num_heads >= 1 and max_positions >= 1 required");
+    if (head_dim < 8 || head_dim > 256 || head_dim % 8 != 0)
+        return fail(PDA_ERR_HEAD_DIM, "head_dim %d must be a multiple of 8 in [8, 256]", head_dim);
+    if (!aligned(x, 16) || !aligned(cos_table, 16) || !aligned(sin_table, 16))
+        return fail(PDA_ERR_ALIGN, "rows and cos/sin tables must be 16-byte aligned");
+    if (!aligned(positions, 4)) return fail(PDA_ERR_ALIGN, "positions must be 4-byte aligned");
+    if (num_tokens > (int64_t(1) << 40) / ((int64_t)num_heads * head_dim))
+        return fail(PDA_ERR_DIMS, "too many elements");
+    return PDA_OK;
+}
+
+}  // namespace
+
+pda_status pda_rope(const void *x, void *out, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, const float *cos_table, const float *sin_table,
+                    int32_t max_positions, const int32_t *positions, void *stream) {
+    clear_err();
+    pda_status st = check_rope_common(x, cos_table, sin_table, positions, num_tokens, num_heads,
+                                      head_dim, max_positions);
+    if (st != PDA_OK) return st;
+    if (!out) return fail(PDA_ERR_NULL, "out is NULL");
+    if (!aligned(out, 16)) return fail(PDA_ERR_ALIGN, "out must be 16-byte aligned");
+    if (num_tokens == 0) return PDA_OK;
+    pda::RopeArgs a{};
+    a.x = static_cast<const uint16_t *>(x);
+    a.out = static_cast<uint16_t *>(out);
+    a.cos_t = cos_table;
+    a.sin_t = sin_table;
+    a.positions = positions;
+    a.T = num_tokens;
+    a.H = num_heads;
+    a.D = head_dim;
+    a.max_pos = max_positions;
+    hipError_t e = pda::launch_rope(a, device_cus(), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "rope launch");
+}
+
+pda_status pda_rope_append_kv(const pda_dims *dims, const void *k_new, const void *v_new,
+                              int64_t num_tokens, const int32_t *token_seq,
+                              const int32_t *positions, const float *cos_table,
+                              const float *sin_table, int32_t max_positions,
+                              const int32_t *block_tables, void *k_pool, void *v_pool,
+                              pda_strides strides, void *stream) {
+    clear_err();
+    pda_status st = check_dims(dims);
+    if (st != PDA_OK) return st;
+    if ((st = check_rope_common(k_new, cos_table, sin_table, positions, num_tokens,
+                                dims->num_kv_heads, dims->head_dim, max_positions)) != PDA_OK)
+        return st;
+    if (!v_new || !token_seq || !block_tables || !k_pool || !v_pool)
+        return fail(PDA_ERR_NULL, "a required pointer is NULL");
+    if (!aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PDA_ERR_ALIGN, "v_new and the pools must be 16-byte aligned");
+    if (!aligned(token_seq, 4) || !aligned(block_tables, 4))
+        return fail(PDA_ERR_ALIGN, "token_seq and block_tables must be 4-byte aligned");
+    if ((st = check_strides(dims, strides)) != PDA_OK) return st;
+    if (num_tokens == 0) return PDA_OK;
+    pda::RopeArgs a{};
+    a.x = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.k_pool = static_cast<uint16_t *>(k_pool);
+    a.v_pool = static_cast<uint16_t *>(v_pool);
+    a.cos_t = cos_table;
+    a.sin_t = sin_table;
+    a.positions = positions;
+    a.token_seq = token_seq;
+    a.blocks = block_tables;
+    a.T = num_tokens;
+    a.blk = strides.blk;
+    a.tok = strides.tok;
+    a.kvh = strides.kvh;
+    a.H = dims->num_kv_heads;
+    a.D = dims->head_dim;
+    a.max_pos = max_positions;
+    a.S = dims->max_seqs;
+    a.cap = dims->tile_capacity;
+    a.bs = dims->block_size;
+    hipError_t e = pda::launch_rope_append_kv(a, device_cus(), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PDA_OK : hip_fail(e, "rope append launch");
 }
 
 pda_status pda_debug_time_attention(void *before, void *after) {

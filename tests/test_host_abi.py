@@ -326,3 +326,41 @@ def test_attn_paged_prefill_rejects_host_tensors():
         pda.attn_paged_prefill(q, kc, kc, bt, lens)
     with pytest.raises(ValueError):
         pda.attn_paged_prefill(q[:, 0], kc, kc, bt, lens)
+
+
+def test_rope_validation_before_enqueue():
+    """pda_rope and pda_rope_append_kv check their arguments before anything
+    is enqueued (addresses are never dereferenced)."""
+    args = dict(x=FAKE, out=FAKE, num_tokens=4, num_heads=2, head_dim=64, cos_table=FAKE,
+                sin_table=FAKE, max_positions=128, positions=FAKE, stream=0)
+    cases = [
+        (dict(x=None), pda.PDA_ERR_NULL), (dict(out=None), pda.PDA_ERR_NULL),
+        (dict(cos_table=None), pda.PDA_ERR_NULL), (dict(positions=None), pda.PDA_ERR_NULL),
+        (dict(head_dim=60), pda.PDA_ERR_HEAD_DIM), (dict(head_dim=264), pda.PDA_ERR_HEAD_DIM),
+        (dict(num_heads=0), pda.PDA_ERR_DIMS), (dict(num_tokens=-1), pda.PDA_ERR_DIMS),
+        (dict(max_positions=0), pda.PDA_ERR_DIMS),
+        (dict(x=FAKE + 8), pda.PDA_ERR_ALIGN), (dict(sin_table=FAKE + 4), pda.PDA_ERR_ALIGN),
+        (dict(positions=FAKE + 2), pda.PDA_ERR_ALIGN),
+    ]
+    for change, status in cases:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_rope(**{**args, **change})
+        assert e.value.status == status, (change, e.value)
+    pda.pda_rope(**{**args, "num_tokens": 0})
+    d = dims()
+    app = dict(dims=d, k_new=FAKE, v_new=FAKE, num_tokens=3, token_seq=FAKE, positions=FAKE,
+               cos_table=FAKE, sin_table=FAKE, max_positions=64, block_tables=FAKE, k_pool=FAKE,
+               v_pool=FAKE, strides=pda.pda_paged_strides(d), stream=0)
+    cases = [
+        (dict(v_new=None), pda.PDA_ERR_NULL), (dict(block_tables=None), pda.PDA_ERR_NULL),
+        (dict(k_pool=None), pda.PDA_ERR_NULL), (dict(token_seq=None), pda.PDA_ERR_NULL),
+        (dict(v_pool=FAKE + 2), pda.PDA_ERR_ALIGN), (dict(token_seq=FAKE + 1), pda.PDA_ERR_ALIGN),
+        (dict(strides=(8, 4, 8)), pda.PDA_ERR_ALIGN),
+        (dict(dims=dims(num_q_heads=6, num_kv_heads=4)), pda.PDA_ERR_GQA),
+        (dict(num_tokens=-2), pda.PDA_ERR_DIMS),
+    ]
+    for change, status in cases:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_rope_append_kv(**{**app, **change})
+        assert e.value.status == status, (change, e.value)
+    pda.pda_rope_append_kv(**{**app, "num_tokens": 0})
