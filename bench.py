@@ -13,7 +13,10 @@ the committed counter summary when the kernel sources still match it.
 
 A prefill workload ("prefill-2048", "prefill-chunk-b16") times one
 pda_prefill call per step instead and reports TFLOP/s against the bf16 MFMA
-peak (the kernel is bound by the matrix cores, not by HBM).
+peak (the kernel is bound by the matrix cores, not by HBM).  "rope-chunk-b16"
+times the rotary step before prefill-chunk-b16's attention: pda_rope over the
+chunk's q rows and pda_rope_append_kv of the chunk's new K/V rows into the
+cache (HBM-bound).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--blocks-per-split N] [--no-cpu-baseline] [--no-kernel-events]
@@ -41,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="ragged-b64",
                     choices=["tiny", "llama3-8b-b16", "ragged-b64", "wide-head-d256", "scratch-b256",
-                             "prefill-2048", "prefill-chunk-b16"])
+                             "prefill-2048", "prefill-chunk-b16", "rope-chunk-b16"])
     ap.add_argument("--rows-per-wave", type=int, default=0, help="prefill: query rows per wave")
     ap.add_argument("--blocks-per-split", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -167,6 +170,9 @@ def main():
     import paged_gqa_decode_pda_amd as pda
 
     log(f"generating workload {args.workload}")
+    if args.workload == "rope-chunk-b16":
+        main_rope(args, workloads.named("prefill-chunk-b16"), torch, pda, torch.device("cuda:0"))
+        return
     w = workloads.named(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -398,6 +404,99 @@ def main_prefill(args, w, torch, pda, dev):
         log("cpu baseline (fp64 oracle, sampled rows)")
         res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def main_rope(args, w, torch, pda, dev):
+    """One step = pda_rope over the chunk's q rows (into a second buffer) and
+    pda_rope_append_kv of one new K row and V row per (chunk token, kv head)
+    at the chunk tokens' positions P - q_len + i."""
+    import oracle
+    S, Q, Hq, D = w.qc.shape
+    Hkv, bs = w.num_kv_heads, w.block_size
+    T = S * Q
+    P = 8192
+    ct, st = oracle.rope_tables(P, D)
+    pos = (w.contexts[:, None] - Q + np.arange(Q)[None, :]).astype(np.int32).reshape(-1)
+    seq = np.repeat(np.arange(S, dtype=np.int32), Q)
+    rng = np.random.Generator(np.random.PCG64(9))
+    kv = torch.from_numpy(workloads_bits(rng, (2, T, Hkv, D)).view(np.int16)).to(dev)
+    qc = torch.from_numpy(w.qc.view(np.int16)).to(dev)
+    qo = torch.empty_like(qc)
+    pool = torch.from_numpy(w.pool.view(np.int16)).to(dev)
+    b, _, _ = w.stacked_tiles()
+    table = torch.from_numpy(b[0]).to(dev)
+    cd, sd = torch.from_numpy(ct).to(dev), torch.from_numpy(st).to(dev)
+    pd, sqd = torch.from_numpy(pos).to(dev), torch.from_numpy(seq).to(dev)
+    dims = pda.pda_dims(S, Hq, Hkv, D, bs, w.tile_capacity)
+    kp, vp = pool.data_ptr() + 2 * w.k_base, pool.data_ptr() + 2 * w.v_base
+    stream = torch.cuda.current_stream()
+
+    def rope_q():
+        pda.pda_rope(qc, qo, T, Hq, D, cd, sd, P, pd, stream)
+
+    def step():
+        rope_q()
+        pda.pda_rope_append_kv(dims, kv[0], kv[1], T, sqd, pd, cd, sd, P, table, kp, vp, w.strides,
+                               stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the rope kernel alone (one launch per pda_rope call), events on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        rope_q()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    rope_us = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e3 / len(evs)
+    tbl = 2 * 4 * (D // 2)                       # one cos and one sin row per token
+    q_bytes = 2 * T * Hq * D * 2 + T * (tbl + 4)
+    kv_bytes = 4 * T * Hkv * D * 2 + T * (tbl + 12)
+    nbytes = q_bytes + kv_bytes
+    tbs = nbytes / (ms * 1e-3) / 1e12
+    achieved = q_bytes / (rope_us * 1e-6) / 1e9
+    res = {
+        "metric": "rotary embedding (q rows + K/V append into the paged cache) achieved HBM TB/s",
+        "value": round(tbs, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "us_per_call": round(ms * 1e3, 2),
+        "pct_of_peak": round(100 * tbs * 1e3 / PEAK_HBM_GBS, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rope-chunk-b16", "tokens": T, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": bs, "max_positions": P,
+                   "algorithmic_bytes": nbytes, "api": "pda_rope + pda_rope_append_kv",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "rope_kernel (q rows), average over event-timed launches",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": q_bytes,
+                     "kernel_us_per_launch": round(rope_us, 2), "launches_per_step": 2},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle)")
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.rope(w.qc.reshape(T, Hq, D), ct, st, pos)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": q_bytes / (el / reps) / 1e12, "unit": "TB/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"q rows of the whole step ({T} tokens x {Hq} heads), "
+                                         f"{reps} repetition(s), fp64 C oracle, one thread"}
+    print(json.dumps(res), flush=True)
+
+
+def workloads_bits(rng, shape):
+    from workloads import f32_to_bf16_bits
+    return f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32))
 
 
 if __name__ == "__main__":
