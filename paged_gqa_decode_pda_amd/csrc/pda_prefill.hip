@@ -45,13 +45,19 @@ constexpr int kPfThreads = 64 * kPfWaves;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// LDS pitch (bytes) of one V row: 16 bytes of padding shift every fourth row
-// by 16 banks.
+// LDS pitch (bytes) of one V row.  A transposing read covers 32 bytes of 16
+// consecutive rows; with 32 bytes of padding each row starts an odd multiple
+// of 8 banks after the previous one, so any 8 consecutive rows take 8
+// disjoint groups of 8 banks.
 template <int DP>
 struct PfTile {
-    static constexpr int kPitch = 2 * DP + 16;
+    static constexpr int kPitch = 2 * DP + 32;
     static constexpr int kBytes = 32 * kPitch;
 };
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -127,6 +133,8 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qd = lane >> 4, col = lane & 15;
     unsigned char *vt = vt_all[w];
+    lds_u8_t *vt_lds = (lds_u8_t *)&vt_all[0][0] + w * PfTile<DP>::kBytes;   // the LDS address space
+    const uint32_t tr_off = (uint32_t)((4 * qd + (col >> 2)) * PITCH + 8 * (col & 3));
 
     // XCD-aware numbering: hardware workgroup b runs on XCD b % 8, so the
     // logical index groups consecutive items on one XCD (the grid is a
@@ -368,26 +376,30 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
                 vkeep = 0;   // decided per element below
         }
         wave_lds_sync();
-        // P.V: A = V^T block n (tokens 4 qd .. +3 of each half, column 16 n + col)
+        // P.V: A = V^T block n, lane (qd, col) holding column 16 n + col of
+        // tokens 4 qd .. 4 qd + 3 of each half.  A transposing LDS read
+        // (ds_read_b64_tr_b16) gives lane i of each 16-lane group element
+        // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
+        // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
+        // 16 n + 4 (c % 4) .. + 3.
 #pragma unroll
         for (int n = 0; n < NDB; ++n) {
-            const unsigned char *base = vt + 2 * (16 * n + col);
-            uint32_t av[4];
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vt_lds + tr_off + 32 * n));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(vt_lds + tr_off + 16 * PITCH + 32 * n));
+            u32x4 A = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+            if constexpr (MASK) {
+                if (vkeep == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r0 = (j < 2 ? 0 : 16) + 4 * qd + 2 * (j & 1);
-                uint32_t lo = *reinterpret_cast<const uint16_t *>(base + r0 * PITCH);
-                uint32_t hi = *reinterpret_cast<const uint16_t *>(base + (r0 + 1) * PITCH);
-                if constexpr (MASK) {
-                    if (vkeep == 0) {
-                        const int bit = 4 * (j >> 1) + 2 * (j & 1);
-                        lo = (keep_any >> bit) & 1 ? lo : 0u;
-                        hi = (keep_any >> (bit + 1)) & 1 ? hi : 0u;
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t m = ((keep_any >> (2 * e)) & 1 ? 0xffffu : 0u) |
+                                           ((keep_any >> (2 * e + 1)) & 1 ? 0xffff0000u : 0u);
+                        A[e] &= m;
                     }
                 }
-                av[j] = lo | (hi << 16);
             }
-            const u32x4 A = {av[0], av[1], av[2], av[3]};
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
