@@ -242,8 +242,9 @@ size_t pda_prefill_workspace_bytes(const pda_dims *dims, int32_t q_len, int32_t 
  *   out           device bf16 [num_seqs, q_len, num_q_heads, head_dim]
  *   blocks_per_split  pages per split-KV partition, 0 = the library's choice
  *   rows_per_wave     16, 32 or 64 query rows (q_len x q-head pairs of one kv
- *                 head) per wavefront, 0 = the library's choice; capped at 16
- *                 for head_dim > 128 and at 32 for head_dim > 64 with a mask
+ *                 head) per wavefront, 0 = the library's choice (16 when a kv
+ *                 head has at most 16 rows, else 32); capped at 16 for
+ *                 head_dim > 128 and at 32 for head_dim > 64 with a mask
  * q head h attends with kv head h / (num_q_heads / num_kv_heads), scale
  * 1/sqrt(head_dim).  A query that keeps no key gets an all-zero row.
  * Device-side contract as pda_decode; with a mask, every row covers the

@@ -474,9 +474,10 @@ pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const
     const int dp = padded_dim(dims->head_dim);
     int rb = rows_per_wave / 16;
     const int max_rb = pda::prefill_max_rb(dp, kv_mask != nullptr);
-    if (rb == 0) {   // the fewest row blocks that cover a kv head's rows, within the instantiated shapes
+    if (rb == 0) {   // 16 rows per wave when they cover a kv head's rows, else 32: at 32
+                     // rows two waves fit each SIMD (64 rows are left to explicit requests)
         const int64_t rows = (int64_t)q_len * G;
-        rb = rows <= 16 ? 1 : (rows <= 32 ? 2 : 4);
+        rb = rows <= 16 ? 1 : 2;
     }
     if (rb > max_rb) rb = max_rb;
     const int32_t ntiles = (int32_t)ceil_div((int64_t)q_len * G, 16 * rb);

@@ -119,8 +119,12 @@ __device__ __forceinline__ u32x4 ld16_at(const uint16_t *base, uint32_t byte_off
     return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
+// Up to 32 rows per wave (head dim up to 128) the registers fit two waves
+// per SIMD (two
+// workgroups per CU), which hide each other's dependency stalls; 64 rows
+// need the whole register file of one wave.
 template <int DP, int RB, bool MASK, bool P16>
-__global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a) {
+__global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) prefill_kernel(const PrefillArgs a) {
     constexpr int NCK = DP / 32;          // 32-element chunks of the head dim
     constexpr int NDB = DP / 16;          // 16-element blocks of the head dim (output)
     constexpr int CPR = DP / 8;           // 16-byte chunks per V row
@@ -234,11 +238,14 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
         return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
     };
 
-    // K of two steps in flight (double-buffered registers); V of the next
-    // step is requested as soon as the current one is in LDS.
-    u32x4 kr[2][2][NCK];   // [buffer][half][chunk]
+    // One register buffer each for K and V: the next step's V is requested
+    // as soon as the current one is in LDS, the next step's K as soon as the
+    // current step's score products have been issued.
+    u32x4 kr[2][NCK];   // [half][chunk]
     u32x4 vr[NV];
-    auto issue_k = [&](int st, int buf) {
+    // The page-id window must cover step st's pages before the first load of
+    // that step is addressed (V of a step is requested before its K).
+    auto window_for = [&](int st) {
         const int tb = t0 + 32 * st;
         const int last = min(tb + 31, t1 - 1);
         if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {   // move the window
@@ -247,12 +254,16 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
             // wait here, so that the path without a move carries no wait
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
+    };
+    auto issue_k = [&](int st) {
+        const int tb = t0 + 32 * st;
+        window_for(st);
         if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const uint16_t *kb = a.k + half_base(tb, hf);
 #pragma unroll
-                for (int c = 0; c < NCK; ++c) kr[buf][hf][c] = ld16_at(kb, kob[c]);
+                for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16_at(kb, kob[c]);
             }
         } else {
 #pragma unroll
@@ -260,12 +271,13 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
                 const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
                 const uint16_t *kp = a.k + row_of(t);
 #pragma unroll
-                for (int c = 0; c < NCK; ++c) kr[buf][hf][c] = ld16(kp + kd[c]);
+                for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16(kp + kd[c]);
             }
         }
     };
     auto issue_v = [&](int st) {
         const int tb = t0 + 32 * st;
+        window_for(st);
         if (P16 && tb + 32 <= t1) {
             const uint16_t *vb[2] = {a.v + half_base(tb, 0), a.v + half_base(tb, 1)};
 #pragma unroll
@@ -282,7 +294,7 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
         }
     };
 
-    auto compute = [&](int st, int buf) {
+    auto compute = [&](int st) {
         const int tb = t0 + 32 * st;
         // V tile into LDS, row-major (columns past head_dim are never stored
         // out), then the next step's V requested into the same registers
@@ -298,21 +310,28 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
         int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
         bool grow = false;
         float alpha[RB];
+        // every row block's score products, then the next step's K into the
+        // same registers
+        f32x4_t sca[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NCK; ++c)
+                    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[hf][c]),
+                                                                __builtin_bit_cast(bf16x8_t, qb[rb][c]), x,
+                                                                0, 0, 0);
+                sca[rb][hf] = x;
+            }
+        }
+        if (st + 1 < nst) issue_k(st + 1);
         auto softmax = [&](auto full_c) {
             constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                f32x4_t sc[2];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int c = 0; c < NCK; ++c)
-                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, kr[buf][hf][c]),
-                            __builtin_bit_cast(bf16x8_t, qb[rb][c]), x, 0, 0, 0);
-                    sc[hf] = x;
-                }
+                f32x4_t sc[2] = {sca[rb][0], sca[rb][1]};
                 // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
                 int keep = 0xff;
                 if constexpr (!FULL) {
@@ -410,17 +429,10 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     };
 
     if (nst > 0) {
-        issue_k(0, 0);
+        issue_k(0);
         issue_v(0);
     }
-    for (int st = 0; st < nst; st += 2) {
-        if (st + 1 < nst) issue_k(st + 1, 1);
-        compute(st, 0);
-        if (st + 1 < nst) {
-            if (st + 2 < nst) issue_k(st + 2, 0);
-            compute(st + 1, 1);
-        }
-    }
+    for (int st = 0; st < nst; ++st) compute(st);
 
     // totals: lane l holds O[row col][16 n + 4 qd + i]
 #pragma unroll
