@@ -88,6 +88,7 @@ def cpu_baseline(w, min_seconds):
 KERNEL_SOURCES = {
     "attend_kernel": ["pda_device.h", "pda_internal.h", "pda_kernels.hip"],
     "prefill_kernel": ["pda_device.h", "pda_internal.h", "pda_prefill.hip"],
+    "rope_kernel": ["pda_device.h", "pda_rope.h", "pda_rope.hip"],
 }
 
 
@@ -474,7 +475,8 @@ def main_rope(args, w, torch, pda, dev):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "rope_kernel (q rows), average over event-timed launches",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": committed_traffic("rope-chunk-b16", "rope_kernel"),
                      "algorithmic_bytes_per_launch": q_bytes,
                      "kernel_us_per_launch": round(rope_us, 2), "launches_per_step": 2},
     }
