@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--mask-drop", type=float, default=None,
                     help="decode with pda_decode_masked and a seeded random keep-mask dropping "
                          "this fraction of positions (single-tile workloads)")
+    ap.add_argument("--decode-via-prefill", action="store_true",
+                    help="decode with pda_prefill at q_len 1 (the matrix-core P.V kernel, each kv "
+                         "head's G q heads padded to 16 rows) instead of pda_decode (single-tile "
+                         "workloads); --blocks-per-split sets its split size")
     return ap.parse_args()
 
 
@@ -205,6 +209,15 @@ def main():
         def step():
             pda.pda_decode_masked(dims, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
                                   w.strides, kv_mask, width, ws, out, bps, stream)
+    elif T == 1 and args.decode_via_prefill:
+        api = "pda_prefill (q_len 1)"
+        pws_n = pda.pda_prefill_workspace_bytes(dims, 1, bps)
+        pws = torch.empty(max(1, (pws_n + 3) // 4), dtype=torch.float32, device=dev) if pws_n else None
+
+        def step():
+            pda.pda_prefill(dims, 1, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
+                            w.strides, True, None, 0, 0, pws, out, bps, 0, stream,
+                            workspace_bytes=pws_n)
     elif T == 1:
         api = "pda_decode"
 
@@ -287,11 +300,13 @@ def main():
     bytes_per_launch = nbytes / launches
     if kernel_us:
         achieved_gbs = bytes_per_launch / (kernel_us * 1e-6) / 1e9
-        kernel_desc = "attend_kernel (paged split-KV attention), average over the timed launches"
+        kernel_desc = ("prefill_kernel at q_len 1" if args.decode_via_prefill else
+                       "attend_kernel (paged split-KV attention)") + ", average over the timed launches"
     else:
         achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
         kernel_desc = f"{api} step (all launches)"
-    traffic = committed_traffic(w.name) if kernel_us and args.mask_drop is None else None
+    traffic = committed_traffic(w.name) if (kernel_us and args.mask_drop is None
+                                            and not args.decode_via_prefill) else None
     res = {
         "metric": "paged decode attention achieved HBM TB/s (K+V+q+out bytes per call / time)",
         "value": round(tbs, 4),
@@ -311,7 +326,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "block_size": w.block_size, "total_tokens": w.total_tokens,
                    "algorithmic_bytes": nbytes, "layout": w.layout, "api": api,
-                   "blocks_per_split": pda.pda_blocks_per_split(dims, bps),
+                   "blocks_per_split": bps if args.decode_via_prefill else pda.pda_blocks_per_split(dims, bps),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kernel_desc,
                      "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
