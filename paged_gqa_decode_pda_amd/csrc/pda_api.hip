@@ -522,6 +522,8 @@ pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const
     a.nsplit = nsplit;
     a.ntiles = ntiles;
     a.causal = causal ? 1 : 0;
+    a.cus = cus;
+    a.longest_first = 0;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dims->head_dim));
     hipError_t e = pda::launch_prefill(a, dp, rb, static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "prefill launch");

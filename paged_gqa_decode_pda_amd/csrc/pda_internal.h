@@ -99,6 +99,8 @@ struct PrefillArgs {
     int32_t nsplit;           // split slots per sequence: ceil(cap bs / span)
     int32_t ntiles;           // row tiles per kv head: ceil(Q G / (16 rb))
     int32_t causal;
+    int32_t cus;              // the device's compute units
+    int32_t longest_first;    // set by the launcher: rank units by length (more workgroups than fit at once)
     float scale_log2;         // log2(e) / sqrt(D)
 };
 

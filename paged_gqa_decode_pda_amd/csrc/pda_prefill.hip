@@ -27,8 +27,10 @@
 // Work items: (sequence, kv split, kv head, row tile) with the row tile
 // fastest; a wave takes one item (RB row blocks of 16 query rows, rows
 // r = i * G + (h - g G) of kv head g) and streams the split's tokens in steps
-// of 32, one step of loads ahead.  Workgroups are renumbered so that
-// consecutive items, which read the same pages, run on one XCD (one L2).
+// of 32, one step of loads ahead.  Units (sequence, kv split, kv head) are
+// dealt round-robin to the eight XCDs, longest first when there are few
+// enough (sequence, split) pairs to rank in each workgroup, and a unit's row
+// tiles, which read the same pages, run on consecutive waves of one XCD.
 // A sequence whose tokens fit one split gets its bf16 result directly;
 // otherwise each item leaves (m, l, o) partials for prefill_merge_kernel.
 #include <type_traits>
@@ -40,6 +42,7 @@ namespace pda {
 namespace {
 
 constexpr int kPfWaves = 4;
+constexpr int kPfSortPairs = 64 * kPfWaves;   // one (sequence, split) pair per thread
 constexpr int kPfThreads = 64 * kPfWaves;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -140,20 +143,48 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
     lds_u8_t *vt_lds = (lds_u8_t *)&vt_all[0][0] + w * PfTile<DP>::kBytes;   // the LDS address space
     const uint32_t tr_off = (uint32_t)((4 * qd + (col >> 2)) * PITCH + 8 * (col & 3));
 
-    // XCD-aware numbering: hardware workgroup b runs on XCD b % 8, so the
-    // logical index groups consecutive items on one XCD (the grid is a
-    // multiple of 8).
-    const int nwg = (int)gridDim.x, b = (int)blockIdx.x;
-    const int lwg = (b & 7) * (nwg >> 3) + (b >> 3);
-    const int64_t item = (int64_t)lwg * kPfWaves + w;
-    const int64_t nitems = (int64_t)a.S * a.nsplit * a.Hkv * a.ntiles;
-    if (item >= nitems) return;
-    const int rt = (int)(item % a.ntiles);
-    int64_t rest = item / a.ntiles;
-    const int g = (int)(rest % a.Hkv);
-    rest /= a.Hkv;
-    const int sp = (int)(rest % a.nsplit);
-    const int s = (int)(rest / a.nsplit);
+    // Work assignment.  Hardware workgroup b runs on XCD b % 8 (the grid is
+    // a multiple of 8).  Units (sequence, split, kv head), kv head fastest,
+    // are dealt round-robin to the XCDs, so each XCD gets an even share of
+    // every sequence; XCD x runs its units in turn, a unit's ntiles row
+    // tiles on consecutive waves (they read the same pages through one L2).
+    // When the workgroups take more than one round of the CUs and there are
+    // at most kPfSortPairs (sequence, split) pairs, the units are taken
+    // longest first, so the launch ends with short work.
+    __shared__ int pair_len[kPfSortPairs];
+    __shared__ int pair_order[kPfSortPairs];
+    const int b = (int)blockIdx.x;
+    const int npairs = a.S * a.nsplit;
+    const bool sorted = a.longest_first != 0 && npairs <= kPfSortPairs;
+    if (sorted) {
+        const int t = threadIdx.x;
+        int len = -1;
+        if (t < npairs) {
+            const int st_ = t / a.nsplit;
+            len = clampi(seq_tokens_pf(a, st_) - (t - st_ * a.nsplit) * a.span, 0, a.span);
+            pair_len[t] = len;
+        }
+        __syncthreads();
+        if (t < npairs) {   // rank by length, descending; ties in index order
+            int rank = 0;
+            for (int j = 0; j < npairs; ++j) {
+                const int lj = pair_len[j];
+                rank += (lj > len || (lj == len && j < t)) ? 1 : 0;
+            }
+            pair_order[rank] = t;
+        }
+        __syncthreads();
+    }
+    const int64_t pos = (int64_t)(b >> 3) * kPfWaves + w;   // position in XCD b % 8's item list
+    const int64_t k = pos / a.ntiles;
+    const int rt = (int)(pos - k * a.ntiles);
+    const int64_t u = (b & 7) + 8 * k;
+    if (u >= (int64_t)npairs * a.Hkv) return;
+    const int g = (int)(u % a.Hkv);
+    int pair = (int)(u / a.Hkv);
+    if (sorted) pair = pair_order[pair];
+    const int sp = pair % a.nsplit;
+    const int s = pair / a.nsplit;
 
     const int P = seq_tokens_pf(a, s);
     const int span = a.span;
@@ -511,10 +542,14 @@ __global__ void __launch_bounds__(kPfThreads) prefill_merge_kernel(const Prefill
 }
 
 template <int DP, int RB, bool MASK, bool P16>
-hipError_t launch_prefill_t(const PrefillArgs &a, hipStream_t st, const AttendEvents &ev) {
-    const int64_t nitems = (int64_t)a.S * a.nsplit * a.Hkv * a.ntiles;
-    int64_t nwg = (nitems + kPfWaves - 1) / kPfWaves;
-    nwg = (nwg + 7) / 8 * 8;
+hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t st, const AttendEvents &ev) {
+    PrefillArgs a = args;
+    // every XCD holds at most ceil(units / 8) units of ntiles items each
+    const int64_t units = (int64_t)a.S * a.nsplit * a.Hkv;
+    const int64_t per_xcd = (units + 7) / 8 * a.ntiles;
+    const int64_t nwg = 8 * ((per_xcd + kPfWaves - 1) / kPfWaves);
+    const int64_t resident = (int64_t)a.cus * ((DP <= 128 && RB <= 2) ? 2 : 1);   // as the launch bounds allow
+    a.longest_first = nwg > resident ? 1 : 0;
     if (ev.before) {
         hipError_t e = hipEventRecord(ev.before, st);
         if (e != hipSuccess) return e;
