@@ -111,6 +111,28 @@ def test_prefill_small_shapes(shape, bps, rpw):
         check(got, ref, case, f"prefill {shape} causal={causal} bps={bps} rpw={rpw}")
 
 
+@pytest.mark.parametrize("order", ["ranked", "unranked"])
+def test_prefill_multi_round_work_orders(order):
+    """Grids that take several rounds of the CUs: with at most 256 (sequence,
+    split) pairs the units are ranked by length in every workgroup (here with
+    KV splits and their merge), with more they keep index order; both are
+    dealt round-robin to the XCDs.  Ragged contexts, causal and not."""
+    announce("prefill multi-round", order)
+    if order == "ranked":   # 40 x 6 pairs, 960 workgroups
+        S, Q, Hq, Hkv, D, cap, bps, hi = 40, 16, 32, 8, 128, 48, 8, 768
+    else:                   # 300 pairs, 1200 workgroups
+        S, Q, Hq, Hkv, D, cap, bps, hi = 300, 16, 32, 8, 64, 13, 0, 208
+    rng = np.random.Generator(np.random.PCG64(61 if order == "ranked" else 62))
+    ctx = rng.integers(Q, hi, endpoint=True, size=S)
+    ctx[::7] = hi   # some full lists
+    case = prefill_case(rng, S, Q, Hq, Hkv, D, 16, ctx, cap=cap)
+    dev = Device(case)
+    for causal in (True, False):
+        got = out_to_f64(run_prefill(dev, case.qc, causal=causal, bps=bps))
+        ref = oracle_prefill(case, causal=causal)["out"]
+        check(got, ref, case, f"prefill {order} causal={causal}")
+
+
 @pytest.mark.parametrize("shape", [SMALL[1], SMALL[3], SMALL[5], SMALL[7]], ids=_ids)
 @pytest.mark.parametrize("ndim", [2, 3])
 def test_prefill_masked(shape, ndim):
