@@ -76,15 +76,35 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // below 2^kRescaleSlack, and the rescale of the accumulators is rare.
 constexpr float kRescaleSlack = 8.f;
 
+// x of lanes l and l^16 (gfx950 v_permlane16_swap of x with itself: the two
+// results hold, per lane, the values of lanes l & ~16 and l | 16), and the
+// same for l^32 (v_permlane32_swap).  VALU lane swaps, no LDS round trip.
+__device__ __forceinline__ void pair16(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
 // Maximum of x over the four lanes l, l^16, l^32, l^48 (one row of the
 // transposed scores).
 __device__ __forceinline__ float max4(float x) {
-    x = fmaxf(x, shfl_xor(x, 16));
-    return fmaxf(x, shfl_xor(x, 32));
+    float a, b;
+    pair16(x, a, b);
+    pair32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
 }
+// Sum over the same four lanes, in an order that is the same in every lane
+// (lanes with bit 4 clear first, then bit 5 clear first).
 __device__ __forceinline__ float sum4(float x) {
-    x += shfl_xor(x, 16);
-    return x + shfl_xor(x, 32);
+    float a, b;
+    pair16(x, a, b);
+    pair32(a + b, a, b);
+    return a + b;
 }
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
@@ -286,13 +306,26 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
     };
+    // The two half bases of the step last addressed: K and V of a step read
+    // the same rows, so the (scalar) address arithmetic is done once per step.
+    int64_t hb[2] = {0, 0};
+    int hb_step = -1;
+    auto bases = [&](int st) {
+        if (hb_step != st) {
+            const int tb = t0 + 32 * st;
+            hb[0] = half_base(tb, 0);
+            hb[1] = half_base(tb, 1);
+            hb_step = st;
+        }
+    };
     auto issue_k = [&](int st) {
         const int tb = t0 + 32 * st;
         window_for(st);
         if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
+            bases(st);
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const uint16_t *kb = a.k + half_base(tb, hf);
+                const uint16_t *kb = a.k + hb[hf];
 #pragma unroll
                 for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16_at(kb, kob[c]);
             }
@@ -310,7 +343,8 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         const int tb = t0 + 32 * st;
         window_for(st);
         if (P16 && tb + 32 <= t1) {
-            const uint16_t *vb[2] = {a.v + half_base(tb, 0), a.v + half_base(tb, 1)};
+            bases(st);
+            const uint16_t *vb[2] = {a.v + hb[0], a.v + hb[1]};
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
