@@ -148,21 +148,16 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x + dpp<kRowRor1>(x);
 }
 
+// Maximum / sum over the whole wave (every lane active), wave-uniform: DPP
+// inside each 16-lane row, then the four row results read into scalars, in
+// one fixed order (no LDS round trip on the chain).
 __device__ __forceinline__ float wave_max(float x) {
-    x = fmaxf(x, shfl_xor(x, 1));
-    x = fmaxf(x, shfl_xor(x, 2));
-    x = fmaxf(x, shfl_xor(x, 4));
-    x = fmaxf(x, shfl_xor(x, 8));
-    x = fmaxf(x, shfl_xor(x, 16));
-    return fmaxf(x, shfl_xor(x, 32));
+    x = row_max16(x);
+    return fmaxf(fmaxf(readlanef(x, 0), readlanef(x, 16)), fmaxf(readlanef(x, 32), readlanef(x, 48)));
 }
 __device__ __forceinline__ float wave_sum(float x) {
-    x += shfl_xor(x, 1);
-    x += shfl_xor(x, 2);
-    x += shfl_xor(x, 4);
-    x += shfl_xor(x, 8);
-    x += shfl_xor(x, 16);
-    return x + shfl_xor(x, 32);
+    x = row_sum16(x);
+    return (readlanef(x, 0) + readlanef(x, 16)) + (readlanef(x, 32) + readlanef(x, 48));
 }
 
 // Softmax weights of one group, moving from the score layout (lane = token)
