@@ -146,7 +146,7 @@ __device__ __forceinline__ u32x4 ld16_at(const uint16_t *base, uint32_t byte_off
 // per SIMD (two
 // workgroups per CU), which hide each other's dependency stalls; 64 rows
 // need the whole register file of one wave.
-template <int DP, int RB, bool MASK, bool P16>
+template <int DP, int RB, bool MASK, bool P16, bool LAPS>
 __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) prefill_kernel(const PrefillArgs a) {
     constexpr int NCK = DP / 32;          // 32-element chunks of the head dim
     constexpr int NDB = DP / 16;          // 16-element blocks of the head dim (output)
@@ -195,339 +195,348 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         }
         __syncthreads();
     }
-    const int64_t pos = (int64_t)(b >> 3) * kPfWaves + w;   // position in XCD b % 8's item list
-    const int64_t k = pos / a.ntiles;
-    const int rt = (int)(pos - k * a.ntiles);
-    const int64_t u = (b & 7) + 8 * k;
-    if (u >= (int64_t)npairs * a.Hkv) return;
-    const int g = (int)(u % a.Hkv);
-    int pair = (int)(u / a.Hkv);
-    if (sorted) pair = pair_order[pair];
-    const int sp = pair % a.nsplit;
-    const int s = pair / a.nsplit;
+    // Each workgroup walks its XCD's list of four-item positions: position
+    // r, then 2R - 1 - r, then 2R + r, ... (R workgroups per XCD, at most
+    // as many as are resident), so no workgroup waits for dispatch and, with
+    // the list longest first, each pairs long work with short.  Without LAPS
+    // (the list fits the resident workgroups) there is one lap.
+    const int R = (int)(gridDim.x >> 3);
+    for (int64_t lap = 0; LAPS || lap == 0; ++lap) {
+        const int64_t r = (lap & 1) ? (R - 1 - (b >> 3)) : (b >> 3);
+        const int64_t pos = (lap * R + r) * kPfWaves + w;   // position in XCD b % 8's item list
+        const int64_t k = pos / a.ntiles;
+        const int rt = (int)(pos - k * a.ntiles);
+        const int64_t u = (b & 7) + 8 * k;
+        if (u >= (int64_t)npairs * a.Hkv) break;   // positions only grow with lap
+        const int g = (int)(u % a.Hkv);
+        int pair = (int)(u / a.Hkv);
+        if (sorted) pair = pair_order[pair];
+        const int sp = pair % a.nsplit;
+        const int s = pair / a.nsplit;
 
-    const int P = seq_tokens_pf(a, s);
-    const int span = a.span;
-    const int nsp = P > 0 ? (P + span - 1) / span : 0;
-    if (sp >= (nsp > 0 ? nsp : 1)) return;
-    const bool direct = nsp <= 1;
+        const int P = seq_tokens_pf(a, s);
+        const int span = a.span;
+        const int nsp = P > 0 ? (P + span - 1) / span : 0;
+        if (sp >= (nsp > 0 ? nsp : 1)) continue;
+        const bool direct = nsp <= 1;
 
-    // this lane's rows, one per row block: r = rt 16 RB + 16 b + col
-    const int QG = a.Q * a.G;
-    int lim[RB];            // last key position the row keeps (-1: none)
-    int64_t rowid[RB];      // (s Q + i) Hq + h, or -1 past the chunk
-    const uint8_t *mrow[RB];  // the row's keep-mask bytes (with a mask)
-    int lim_max = -1, lim_min = 0x7fffffff;
-    u32x4 qb[RB][NCK];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int r = rt * 16 * RB + 16 * rb + col;
-        const bool ok = r < QG;
-        const int i = ok ? r / a.G : 0;
-        const int h = g * a.G + (ok ? r - i * a.G : 0);
-        rowid[rb] = ok ? ((int64_t)s * a.Q + i) * a.Hq + h : -1;
-        lim[rb] = ok ? (a.causal ? P - a.Q + i : P - 1) : -1;
-        mrow[rb] = MASK ? a.mask + (int64_t)s * a.mask_ss + (int64_t)i * a.mask_qs : nullptr;
-        lim_max = max(lim_max, lim[rb]);
-        if (ok) lim_min = min(lim_min, lim[rb]);
-        const uint16_t *qp = a.q + (ok ? rowid[rb] : 0) * a.D;
-#pragma unroll
+        // this lane's rows, one per row block: r = rt 16 RB + 16 b + col
+        const int QG = a.Q * a.G;
+        int lim[RB];            // last key position the row keeps (-1: none)
+        int64_t rowid[RB];      // (s Q + i) Hq + h, or -1 past the chunk
+        const uint8_t *mrow[RB];  // the row's keep-mask bytes (with a mask)
+        int lim_max = -1, lim_min = 0x7fffffff;
+        u32x4 qb[RB][NCK];
+    #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int r = rt * 16 * RB + 16 * rb + col;
+            const bool ok = r < QG;
+            const int i = ok ? r / a.G : 0;
+            const int h = g * a.G + (ok ? r - i * a.G : 0);
+            rowid[rb] = ok ? ((int64_t)s * a.Q + i) * a.Hq + h : -1;
+            lim[rb] = ok ? (a.causal ? P - a.Q + i : P - 1) : -1;
+            mrow[rb] = MASK ? a.mask + (int64_t)s * a.mask_ss + (int64_t)i * a.mask_qs : nullptr;
+            lim_max = max(lim_max, lim[rb]);
+            if (ok) lim_min = min(lim_min, lim[rb]);
+            const uint16_t *qp = a.q + (ok ? rowid[rb] : 0) * a.D;
+    #pragma unroll
+            for (int c = 0; c < NCK; ++c) {
+                const int d0 = 32 * c + 8 * qd;
+                qb[rb][c] = (ok && d0 < a.D) ? ld16(qp + d0) : u32x4{0, 0, 0, 0};
+            }
+        }
+        lim_max = __builtin_amdgcn_readfirstlane(wave_max_i(lim_max));
+        lim_min = __builtin_amdgcn_readfirstlane(wave_min_i(lim_min));
+
+        const int t0 = sp * span;
+        const int t1 = min(min(t0 + span, P), lim_max + 1);
+        const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+
+        float m2[RB], lsum[RB];
+        f32x4_t acc[RB][NDB];
+    #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            m2[rb] = -INFINITY;
+            lsum[rb] = 0.f;
+    #pragma unroll
+            for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+        const int32_t *brow = a.blocks + (int64_t)s * a.cap;
+        const int64_t gk = (int64_t)g * a.kvh;
+        int cb = t0 / a.bs;   // first page of the page-id window
+        int bidvec = brow[min(cb + lane, a.cap - 1)];
+        int kd[NCK];
+    #pragma unroll
         for (int c = 0; c < NCK; ++c) {
             const int d0 = 32 * c + 8 * qd;
-            qb[rb][c] = (ok && d0 < a.D) ? ld16(qp + d0) : u32x4{0, 0, 0, 0};
+            kd[c] = d0 < a.D ? d0 : 0;   // past head_dim: re-read chunk 0 (q is 0 there)
         }
-    }
-    lim_max = __builtin_amdgcn_readfirstlane(wave_max_i(lim_max));
-    lim_min = __builtin_amdgcn_readfirstlane(wave_min_i(lim_min));
+        const int vrow = lane / CPR;           // V row within a load instruction
+        const int vd = (lane % CPR) * 8;       // first V element of the lane
+        const int vdo = vd < a.D ? vd : 0;
+        // lane byte offsets from a page row's start, for steps whose 16-token
+        // halves each lie inside one page (block_size a multiple of 16)
+        uint32_t kob[NCK];
+    #pragma unroll
+        for (int c = 0; c < NCK; ++c) kob[c] = 2u * (uint32_t)(col * (int)a.tok + kd[c]);
+        const uint32_t vob = 2u * (uint32_t)(vrow * (int)a.tok + vdo);
+        // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
+        // 16-aligned and listed
+        auto half_base = [&](int tb, int hf) -> int64_t {
+            const int th = tb + 16 * hf;
+            const int pg = page_of((uint32_t)th, a.bs_magic);
+            const int bid = __builtin_amdgcn_readlane(bidvec, pg - cb);
+            return (int64_t)bid * a.blk + gk + (int64_t)(th - pg * a.bs) * a.tok;
+        };
 
-    const int t0 = sp * span;
-    const int t1 = min(min(t0 + span, P), lim_max + 1);
-    const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
+        // Element offset of token t's row (kv head g); t must be listed.
+        auto row_of = [&](int t) -> int64_t {
+            const int pg = page_of((uint32_t)t, a.bs_magic);
+            const int bid = __shfl(bidvec, pg - cb, 64);
+            return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
+        };
 
-    float m2[RB], lsum[RB];
-    f32x4_t acc[RB][NDB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        m2[rb] = -INFINITY;
-        lsum[rb] = 0.f;
-#pragma unroll
-        for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const int32_t *brow = a.blocks + (int64_t)s * a.cap;
-    const int64_t gk = (int64_t)g * a.kvh;
-    int cb = t0 / a.bs;   // first page of the page-id window
-    int bidvec = brow[min(cb + lane, a.cap - 1)];
-    int kd[NCK];
-#pragma unroll
-    for (int c = 0; c < NCK; ++c) {
-        const int d0 = 32 * c + 8 * qd;
-        kd[c] = d0 < a.D ? d0 : 0;   // past head_dim: re-read chunk 0 (q is 0 there)
-    }
-    const int vrow = lane / CPR;           // V row within a load instruction
-    const int vd = (lane % CPR) * 8;       // first V element of the lane
-    const int vdo = vd < a.D ? vd : 0;
-    // lane byte offsets from a page row's start, for steps whose 16-token
-    // halves each lie inside one page (block_size a multiple of 16)
-    uint32_t kob[NCK];
-#pragma unroll
-    for (int c = 0; c < NCK; ++c) kob[c] = 2u * (uint32_t)(col * (int)a.tok + kd[c]);
-    const uint32_t vob = 2u * (uint32_t)(vrow * (int)a.tok + vdo);
-    // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
-    // 16-aligned and listed
-    auto half_base = [&](int tb, int hf) -> int64_t {
-        const int th = tb + 16 * hf;
-        const int pg = page_of((uint32_t)th, a.bs_magic);
-        const int bid = __builtin_amdgcn_readlane(bidvec, pg - cb);
-        return (int64_t)bid * a.blk + gk + (int64_t)(th - pg * a.bs) * a.tok;
-    };
-
-    // Element offset of token t's row (kv head g); t must be listed.
-    auto row_of = [&](int t) -> int64_t {
-        const int pg = page_of((uint32_t)t, a.bs_magic);
-        const int bid = __shfl(bidvec, pg - cb, 64);
-        return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
-    };
-
-    // One register buffer each for K and V: the next step's V is requested
-    // as soon as the current one is in LDS, the next step's K as soon as the
-    // current step's score products have been issued.
-    u32x4 kr[2][NCK];   // [half][chunk]
-    u32x4 vr[NV];
-    // The page-id window must cover step st's pages before the first load of
-    // that step is addressed (V of a step is requested before its K).
-    auto window_for = [&](int st) {
-        const int tb = t0 + 32 * st;
-        const int last = min(tb + 31, t1 - 1);
-        if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {   // move the window
-            cb = page_of((uint32_t)tb, a.bs_magic);
-            bidvec = brow[min(cb + lane, a.cap - 1)];
-            // wait here, so that the path without a move carries no wait
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        }
-    };
-    // The two half bases of the step last addressed: K and V of a step read
-    // the same rows, so the (scalar) address arithmetic is done once per step.
-    int64_t hb[2] = {0, 0};
-    int hb_step = -1;
-    auto bases = [&](int st) {
-        if (hb_step != st) {
+        // One register buffer each for K and V: the next step's V is requested
+        // as soon as the current one is in LDS, the next step's K as soon as the
+        // current step's score products have been issued.
+        u32x4 kr[2][NCK];   // [half][chunk]
+        u32x4 vr[NV];
+        // The page-id window must cover step st's pages before the first load of
+        // that step is addressed (V of a step is requested before its K).
+        auto window_for = [&](int st) {
             const int tb = t0 + 32 * st;
-            hb[0] = half_base(tb, 0);
-            hb[1] = half_base(tb, 1);
-            hb_step = st;
-        }
-    };
-    auto issue_k = [&](int st) {
-        const int tb = t0 + 32 * st;
-        window_for(st);
-        if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
-            bases(st);
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const uint16_t *kb = a.k + hb[hf];
-#pragma unroll
-                for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16_at(kb, kob[c]);
-            }
-        } else {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
-                const uint16_t *kp = a.k + row_of(t);
-#pragma unroll
-                for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16(kp + kd[c]);
-            }
-        }
-    };
-    auto issue_v = [&](int st) {
-        const int tb = t0 + 32 * st;
-        window_for(st);
-        if (P16 && tb + 32 <= t1) {
-            bases(st);
-            const uint16_t *vb[2] = {a.v + hb[0], a.v + hb[1]};
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
-                vr[v] = ld16_at(vb[hf] + (int64_t)r0 * a.tok, vob);
-            }
-        } else {
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int t = min(tb + RPI * v + vrow, t1 - 1);
-                vr[v] = ld16(a.v + row_of(t) + vdo);
-            }
-        }
-    };
-
-    auto compute = [&](int st) {
-        const int tb = t0 + 32 * st;
-        // V tile into LDS, row-major (columns past head_dim are never stored
-        // out), then the next step's V requested into the same registers
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-            *reinterpret_cast<u32x4 *>(vt + (RPI * v + vrow) * PITCH + 2 * vd) = vr[v];
-        if (st + 1 < nst) issue_v(st + 1);
-        // scores, transposed: lane -> row col, tokens 16 hf + 4 qd + i.  A
-        // step inside every row's range (and the split's) keeps all tokens
-        // and takes the path without per-token tests.
-        const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
-        u32x4 pb[RB];
-        int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
-        bool grow = false;
-        float alpha[RB];
-        // every row block's score products, then the next step's K into the
-        // same registers
-        f32x4_t sca[RB][2];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < NCK; ++c)
-                    x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[hf][c]),
-                                                                __builtin_bit_cast(bf16x8_t, qb[rb][c]), x,
-                                                                0, 0, 0);
-                sca[rb][hf] = x;
-            }
-        }
-        if (st + 1 < nst) issue_k(st + 1);
-        auto softmax = [&](auto full_c) {
-            constexpr bool FULL = decltype(full_c)::value;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                f32x4_t sc[2] = {sca[rb][0], sca[rb][1]};
-                // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
-                int keep = 0xff;
-                if constexpr (!FULL) {
-                    keep = 0;
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int t = tb + 16 * hf + 4 * qd + i;
-                            bool ok = t < t1 && t <= lim[rb];
-                            if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
-                            keep |= ok ? 1 << (4 * hf + i) : 0;
-                            sc[hf][i] = ok ? sc[hf][i] : -INFINITY;
-                        }
-                    }
-                    keep_any |= keep;
-                }
-                float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-                mx = max4(mx) * a.scale_log2;
-                // move the reference max only when the row's max passes it by
-                // more than the slack (a row with nothing kept so far keeps
-                // (m, l, o) = (-inf, 0, 0))
-                const bool mv = mx > m2[rb] + kRescaleSlack;
-                const float mn = mv ? mx : m2[rb];
-                alpha[rb] = mv ? exp2_fast(m2[rb] - mn) : 1.f;
-                grow |= mv;
-                m2[rb] = mn;
-                float p[8];
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float e = exp2_fast(fmaf(sc[hf][i], a.scale_log2, -mn));
-                        p[4 * hf + i] = FULL || ((keep >> (4 * hf + i)) & 1) ? e : 0.f;
-                    }
-                }
-                pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                               pack_bf16(p[6], p[7])};
-                // l sums the weights as rounded for the product
-                float ps = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ps += bf_lo(pb[rb][e]) + bf_hi(pb[rb][e]);
-                lsum[rb] = fmaf(lsum[rb], alpha[rb], ps);
+            const int last = min(tb + 31, t1 - 1);
+            if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {   // move the window
+                cb = page_of((uint32_t)tb, a.bs_magic);
+                bidvec = brow[min(cb + lane, a.cap - 1)];
+                // wait here, so that the path without a move carries no wait
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         };
-        if (full) softmax(std::true_type{});
-        else softmax(std::false_type{});
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-                for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
+        // The two half bases of the step last addressed: K and V of a step read
+        // the same rows, so the (scalar) address arithmetic is done once per step.
+        int64_t hb[2] = {0, 0};
+        int hb_step = -1;
+        auto bases = [&](int st) {
+            if (hb_step != st) {
+                const int tb = t0 + 32 * st;
+                hb[0] = half_base(tb, 0);
+                hb[1] = half_base(tb, 1);
+                hb_step = st;
             }
-        }
-        // tokens no row keeps get V = 0 (with a mask they may hold anything)
-        uint32_t vkeep = 0xffffffffu;
-        if constexpr (MASK) {
-            keep_any = or16(keep_any);
-            if (__builtin_amdgcn_ballot_w64(keep_any != 0xff) != 0)
-                vkeep = 0;   // decided per element below
-        }
-        wave_lds_sync();
-        // P.V: A = V^T block n, lane (qd, col) holding column 16 n + col of
-        // tokens 4 qd .. 4 qd + 3 of each half.  A transposing LDS read
-        // (ds_read_b64_tr_b16) gives lane i of each 16-lane group element
-        // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
-        // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
-        // 16 n + 4 (c % 4) .. + 3.
-#pragma unroll
-        for (int n = 0; n < NDB; ++n) {
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vt_lds + tr_off + 32 * n));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t *)(vt_lds + tr_off + 16 * PITCH + 32 * n));
-            u32x4 A = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+        };
+        auto issue_k = [&](int st) {
+            const int tb = t0 + 32 * st;
+            window_for(st);
+            if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
+                bases(st);
+    #pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const uint16_t *kb = a.k + hb[hf];
+    #pragma unroll
+                    for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16_at(kb, kob[c]);
+                }
+            } else {
+    #pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
+                    const uint16_t *kp = a.k + row_of(t);
+    #pragma unroll
+                    for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16(kp + kd[c]);
+                }
+            }
+        };
+        auto issue_v = [&](int st) {
+            const int tb = t0 + 32 * st;
+            window_for(st);
+            if (P16 && tb + 32 <= t1) {
+                bases(st);
+                const uint16_t *vb[2] = {a.v + hb[0], a.v + hb[1]};
+    #pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
+                    vr[v] = ld16_at(vb[hf] + (int64_t)r0 * a.tok, vob);
+                }
+            } else {
+    #pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    const int t = min(tb + RPI * v + vrow, t1 - 1);
+                    vr[v] = ld16(a.v + row_of(t) + vdo);
+                }
+            }
+        };
+
+        auto compute = [&](int st) {
+            const int tb = t0 + 32 * st;
+            // V tile into LDS, row-major (columns past head_dim are never stored
+            // out), then the next step's V requested into the same registers
+    #pragma unroll
+            for (int v = 0; v < NV; ++v)
+                *reinterpret_cast<u32x4 *>(vt + (RPI * v + vrow) * PITCH + 2 * vd) = vr[v];
+            if (st + 1 < nst) issue_v(st + 1);
+            // scores, transposed: lane -> row col, tokens 16 hf + 4 qd + i.  A
+            // step inside every row's range (and the split's) keeps all tokens
+            // and takes the path without per-token tests.
+            const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
+            u32x4 pb[RB];
+            int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
+            bool grow = false;
+            float alpha[RB];
+            // every row block's score products, then the next step's K into the
+            // same registers
+            f32x4_t sca[RB][2];
+    #pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+    #pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+    #pragma unroll
+                    for (int c = 0; c < NCK; ++c)
+                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[hf][c]),
+                                                                    __builtin_bit_cast(bf16x8_t, qb[rb][c]), x,
+                                                                    0, 0, 0);
+                    sca[rb][hf] = x;
+                }
+            }
+            if (st + 1 < nst) issue_k(st + 1);
+            auto softmax = [&](auto full_c) {
+                constexpr bool FULL = decltype(full_c)::value;
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    f32x4_t sc[2] = {sca[rb][0], sca[rb][1]};
+                    // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
+                    int keep = 0xff;
+                    if constexpr (!FULL) {
+                        keep = 0;
+    #pragma unroll
+                        for (int hf = 0; hf < 2; ++hf) {
+    #pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int t = tb + 16 * hf + 4 * qd + i;
+                                bool ok = t < t1 && t <= lim[rb];
+                                if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
+                                keep |= ok ? 1 << (4 * hf + i) : 0;
+                                sc[hf][i] = ok ? sc[hf][i] : -INFINITY;
+                            }
+                        }
+                        keep_any |= keep;
+                    }
+                    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+                    mx = max4(mx) * a.scale_log2;
+                    // move the reference max only when the row's max passes it by
+                    // more than the slack (a row with nothing kept so far keeps
+                    // (m, l, o) = (-inf, 0, 0))
+                    const bool mv = mx > m2[rb] + kRescaleSlack;
+                    const float mn = mv ? mx : m2[rb];
+                    alpha[rb] = mv ? exp2_fast(m2[rb] - mn) : 1.f;
+                    grow |= mv;
+                    m2[rb] = mn;
+                    float p[8];
+    #pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float e = exp2_fast(fmaf(sc[hf][i], a.scale_log2, -mn));
+                            p[4 * hf + i] = FULL || ((keep >> (4 * hf + i)) & 1) ? e : 0.f;
+                        }
+                    }
+                    pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
+                                   pack_bf16(p[6], p[7])};
+                    // l sums the weights as rounded for the product
+                    float ps = 0.f;
+    #pragma unroll
+                    for (int e = 0; e < 4; ++e) ps += bf_lo(pb[rb][e]) + bf_hi(pb[rb][e]);
+                    lsum[rb] = fmaf(lsum[rb], alpha[rb], ps);
+                }
+            };
+            if (full) softmax(std::true_type{});
+            else softmax(std::false_type{});
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+    #pragma unroll
+                    for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
+                }
+            }
+            // tokens no row keeps get V = 0 (with a mask they may hold anything)
+            uint32_t vkeep = 0xffffffffu;
             if constexpr (MASK) {
-                if (vkeep == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t m = ((keep_any >> (2 * e)) & 1 ? 0xffffu : 0u) |
-                                           ((keep_any >> (2 * e + 1)) & 1 ? 0xffff0000u : 0u);
-                        A[e] &= m;
+                keep_any = or16(keep_any);
+                if (__builtin_amdgcn_ballot_w64(keep_any != 0xff) != 0)
+                    vkeep = 0;   // decided per element below
+            }
+            wave_lds_sync();
+            // P.V: A = V^T block n, lane (qd, col) holding column 16 n + col of
+            // tokens 4 qd .. 4 qd + 3 of each half.  A transposing LDS read
+            // (ds_read_b64_tr_b16) gives lane i of each 16-lane group element
+            // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
+            // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
+            // 16 n + 4 (c % 4) .. + 3.
+    #pragma unroll
+            for (int n = 0; n < NDB; ++n) {
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(vt_lds + tr_off + 32 * n));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t *)(vt_lds + tr_off + 16 * PITCH + 32 * n));
+                u32x4 A = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
+                if constexpr (MASK) {
+                    if (vkeep == 0) {
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t m = ((keep_any >> (2 * e)) & 1 ? 0xffffu : 0u) |
+                                               ((keep_any >> (2 * e + 1)) & 1 ? 0xffff0000u : 0u);
+                            A[e] &= m;
+                        }
                     }
                 }
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                                         __builtin_bit_cast(bf16x8_t, pb[rb]),
+                                                                         acc[rb][n], 0, 0, 0);
             }
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
-                                                                     __builtin_bit_cast(bf16x8_t, pb[rb]),
-                                                                     acc[rb][n], 0, 0, 0);
+            wave_lds_sync();
+        };
+
+        if (nst > 0) {
+            issue_k(0);
+            issue_v(0);
         }
-        wave_lds_sync();
-    };
+        for (int st = 0; st < nst; ++st) compute(st);
 
-    if (nst > 0) {
-        issue_k(0);
-        issue_v(0);
-    }
-    for (int st = 0; st < nst; ++st) compute(st);
-
-    // totals: lane l holds O[row col][16 n + 4 qd + i]
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const float L = sum4(lsum[rb]);
-        if (rowid[rb] < 0) continue;
-        if (direct) {
-            uint16_t *op = a.out + rowid[rb] * a.D;
-            const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-            for (int n = 0; n < NDB; ++n) {
-                const int d = 16 * n + 4 * qd;
-                if (d >= a.D) continue;
-                const f32x4_t x = acc[rb][n];
-                *reinterpret_cast<u32x2 *>(op + d) =
-                    u32x2{pack_bf16(x[0] * inv, x[1] * inv), pack_bf16(x[2] * inv, x[3] * inv)};
-            }
-        } else {
-            const int64_t pi = rowid[rb] * a.nsplit + sp;
-            if (L > 0.f) {
-                float *po = a.part_o + pi * a.D;
-#pragma unroll
+        // totals: lane l holds O[row col][16 n + 4 qd + i]
+    #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float L = sum4(lsum[rb]);
+            if (rowid[rb] < 0) continue;
+            if (direct) {
+                uint16_t *op = a.out + rowid[rb] * a.D;
+                const float inv = L > 0.f ? 1.f / L : 0.f;
+    #pragma unroll
                 for (int n = 0; n < NDB; ++n) {
                     const int d = 16 * n + 4 * qd;
-                    if (d < a.D) *reinterpret_cast<f32x4_t *>(po + d) = acc[rb][n];
+                    if (d >= a.D) continue;
+                    const f32x4_t x = acc[rb][n];
+                    *reinterpret_cast<u32x2 *>(op + d) =
+                        u32x2{pack_bf16(x[0] * inv, x[1] * inv), pack_bf16(x[2] * inv, x[3] * inv)};
                 }
-            }
-            if (qd == 0) {
-                a.part_ml[2 * pi] = m2[rb];
-                a.part_ml[2 * pi + 1] = L;
+            } else {
+                const int64_t pi = rowid[rb] * a.nsplit + sp;
+                if (L > 0.f) {
+                    float *po = a.part_o + pi * a.D;
+    #pragma unroll
+                    for (int n = 0; n < NDB; ++n) {
+                        const int d = 16 * n + 4 * qd;
+                        if (d < a.D) *reinterpret_cast<f32x4_t *>(po + d) = acc[rb][n];
+                    }
+                }
+                if (qd == 0) {
+                    a.part_ml[2 * pi] = m2[rb];
+                    a.part_ml[2 * pi + 1] = L;
+                }
             }
         }
     }
@@ -578,17 +587,23 @@ __global__ void __launch_bounds__(kPfThreads) prefill_merge_kernel(const Prefill
 template <int DP, int RB, bool MASK, bool P16>
 hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t st, const AttendEvents &ev) {
     PrefillArgs a = args;
-    // every XCD holds at most ceil(units / 8) units of ntiles items each
+    // every XCD holds at most ceil(units / 8) units of ntiles items each; at
+    // most as many workgroups as are resident, each looping over positions
     const int64_t units = (int64_t)a.S * a.nsplit * a.Hkv;
     const int64_t per_xcd = (units + 7) / 8 * a.ntiles;
-    const int64_t nwg = 8 * ((per_xcd + kPfWaves - 1) / kPfWaves);
-    const int64_t resident = (int64_t)a.cus * ((DP <= 128 && RB <= 2) ? 2 : 1);   // as the launch bounds allow
-    a.longest_first = nwg > resident ? 1 : 0;
+    const int64_t need = (per_xcd + kPfWaves - 1) / kPfWaves;   // positions per XCD
+    const int64_t per_cu = (DP <= 128 && RB <= 2) ? 2 : 1;      // as the launch bounds allow
+    const int64_t resident = (a.cus >= 8 ? a.cus / 8 : 1) * per_cu;   // per XCD
+    const int64_t nwg = 8 * (need < resident ? need : resident);
+    a.longest_first = need > resident ? 1 : 0;
     if (ev.before) {
         hipError_t e = hipEventRecord(ev.before, st);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((prefill_kernel<DP, RB, MASK, P16>), dim3((unsigned)nwg), dim3(kPfThreads), 0, st, a);
+    if (need > resident)
+        hipLaunchKernelGGL((prefill_kernel<DP, RB, MASK, P16, true>), dim3((unsigned)nwg), dim3(kPfThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<DP, RB, MASK, P16, false>), dim3((unsigned)nwg), dim3(kPfThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev.after) {
