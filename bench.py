@@ -5,11 +5,22 @@ kernel) over the ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
 head_dim 128, block_size 16, contexts log-uniform in [128, 32768], 1 % of keys
 scaled by 4, paged layout (workload "ragged-b64"; the other named workloads
 run the same way, tiled ones as begin_step + step_tile per tile + finalize).  Inputs
-are seeded synthetic bf16, resident in HBM before the timed region.  Prints
-one JSON line: `value` from the timed steps; `roofline.achieved` from the
-attention kernel's own average duration, taken with an event pair around each
-of its launches in a second pass over the same steps; `roofline.traffic` from
-the committed counter summary when the kernel sources still match it.
+are seeded synthetic bf16, resident in HBM before the timed region.
+
+Timing protocol (every workload): the W warm-up steps asked for, then more
+warm-up until the GPU runs at its steady rate (at least --min-warmup-ms of
+steps, and two consecutive windows of >= 20 ms whose per-step times agree
+within 2 %: after an idle period the first tens of milliseconds run up to
+20 % slower while the clocks settle); then exactly K steps bracketed by
+device synchronisations give `value` and `ms_per_step`; then 5 batches of
+>= --batch-ms each (event-timed on the launch stream) give the median and
+spread in `steady_state`.  `roofline.achieved` comes from the attention
+kernel's own average duration, taken with an event pair around each of its
+launches in a further pass over K steps; `roofline.traffic` from the
+committed counter summary when the kernel sources still match it.  A
+workload whose K/V bytes would sit in the 256 MB last-level cache
+(llama3-8b-b16) rotates over enough copies of its pool (>= 7, >= 1 GiB) that
+every step reads from HBM.
 
 A prefill workload ("prefill-2048", "prefill-chunk-b16") times one
 pda_prefill call per step instead and reports TFLOP/s against the bf16 MFMA
@@ -47,6 +58,14 @@ def parse():
                              "prefill-2048", "prefill-chunk-b16", "rope-chunk-b16"])
     ap.add_argument("--rows-per-wave", type=int, default=0, help="prefill: query rows per wave")
     ap.add_argument("--blocks-per-split", type=int, default=0)
+    ap.add_argument("--min-warmup-ms", type=float, default=300.0,
+                    help="warm up for at least this long (after the --warmup steps) and until the "
+                         "per-step time is steady")
+    ap.add_argument("--batch-ms", type=float, default=50.0,
+                    help="length of each of the 5 steady-state batches")
+    ap.add_argument("--rotate", type=int, default=-1,
+                    help="pool copies to rotate over, one per step (-1: automatic, enough copies "
+                         "for >= 1 GiB when the pool fits in the last-level cache; 0 or 1: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -70,21 +89,122 @@ def log(*a):
 
 def cpu_baseline(w, min_seconds):
     """The fp64 oracle as it stands, on the host cores, over the whole workload
-    (repeated until `min_seconds` have passed), in the metric's unit."""
+    (repeated until `min_seconds` have passed), in the metric's unit.  The
+    small workloads (tiny, llama3-8b-b16) also get a one-thread figure."""
     import oracle
     threads = oracle.host_threads()
-    reps, t0 = 0, time.perf_counter()
+
+    def run(nthreads, seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.attend_workload(w, threads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return el / reps, reps
+
+    per, reps = run(threads, min_seconds)
+    res = {"value": w.algorithmic_bytes() / per / 1e12, "unit": "TB/s", "cores": threads,
+           "kind": "oracle", "us_per_call": per * 1e6, "cpu_model": cpu_model(),
+           "sample": f"whole workload ({w.num_seqs * w.num_q_heads} (sequence, q head) pairs), "
+                     f"{reps} repetition(s), fp64 C oracle with OpenMP"}
+    if w.name in ("tiny", "llama3-8b-b16") and threads > 1:
+        per1, reps1 = run(1, min_seconds / 2)
+        res["single_core"] = {"value": w.algorithmic_bytes() / per1 / 1e12, "unit": "TB/s",
+                              "us_per_call": per1 * 1e6, "repetitions": reps1}
+    return res
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measure(args, torch, stream, step):
+    """Steady-state timing of `step` (one call = one step, enqueued on `stream`).
+
+    1. the --warmup steps asked for;
+    2. more warm-up in windows of >= 20 ms (event-timed) until at least
+       --min-warmup-ms has passed and two consecutive windows agree within
+       2 % per step (at most 5 s);
+    3. exactly --steps steps bracketed by device synchronisations (wall
+       clock; also an event pair on the stream);
+    4. 5 batches of >= --batch-ms each, event-timed.
+    Returns a dict of the figures (times in microseconds per step)."""
+    sync = torch.cuda.synchronize
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(n):
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(n):
+            step()
+        b.record(stream)
+        sync()
+        return a.elapsed_time(b) * 1e3 / n
+
+    for _ in range(args.warmup):
+        step()
+    sync()
+    t_est = timed(3)
+    n_win = max(3, int(np.ceil(20e3 / max(t_est, 1.0))))
+    extra, spent_us, prev, converged = 3, 3 * t_est, None, False
     while True:
-        oracle.attend_workload(w, threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
+        t = timed(n_win)
+        extra += n_win
+        spent_us += n_win * t
+        if prev is not None and abs(t - prev) <= 0.02 * prev and spent_us >= args.min_warmup_ms * 1e3:
+            converged = True
             break
-    per = el / reps
-    return {"value": w.algorithmic_bytes() / per / 1e12, "unit": "TB/s", "cores": threads,
-            "kind": "oracle", "us_per_call": per * 1e6,
-            "sample": f"whole workload ({w.num_seqs * w.num_q_heads} (sequence, q head) pairs), "
-                      f"{reps} repetition(s), fp64 C oracle with OpenMP"}
+        if spent_us >= 5e6:
+            break
+        prev = t
+    log(f"warm-up: {args.warmup} + {extra} steps, {spent_us / 1e3:.0f} ms, last window {t:.1f} us/step")
+
+    log(f"timing {args.steps} steps")
+    e0, e1 = ev(), ev()
+    sync()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    sync()
+    wall_us = (time.perf_counter() - t0) * 1e6 / args.steps
+    event_us = e0.elapsed_time(e1) * 1e3 / args.steps
+
+    n_b = max(1, int(np.ceil(args.batch_ms * 1e3 / max(t, 1.0))))
+    log(f"5 batches of {n_b} steps")
+    batches = [timed(n_b) for _ in range(5)]
+    med = float(np.median(batches))
+    return {"wall_us": wall_us, "event_us": event_us, "warmup_extra_steps": extra,
+            "warmup_ms": spent_us / 1e3, "warmup_converged": converged,
+            "batch_steps": n_b, "batch_us": batches, "batch_median_us": med,
+            "batch_spread_pct": 100.0 * (max(batches) - min(batches)) / med}
+
+
+def steady_fields(m, per_step_amount, unit, scale):
+    """The JSON fields of the warm-up and the 5 steady-state batches."""
+    med = m["batch_median_us"]
+    return {
+        "warmup_extra_steps": m["warmup_extra_steps"],
+        "warmup_ms": round(m["warmup_ms"], 1),
+        "warmup_converged": m["warmup_converged"],
+        "event_us_per_step": round(m["event_us"], 2),
+        "steady_state": {"batches": 5, "steps_per_batch": m["batch_steps"],
+                         "us_per_step_median": round(med, 2),
+                         "us_per_step_min": round(min(m["batch_us"]), 2),
+                         "us_per_step_max": round(max(m["batch_us"]), 2),
+                         "spread_pct": round(m["batch_spread_pct"], 2),
+                         "value_median": round(per_step_amount / (med * 1e-6) / scale, 4),
+                         "unit": unit},
+    }
 
 
 # The sources each kernel's code and launch come from (a committed counter
@@ -127,7 +247,7 @@ def cpu_baseline_prefill(w, min_seconds, sample_rows=4096):
             break
     per = el / reps
     return {"value": flops / per / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows.size} seeded (sequence, query, q head) rows of {S * Q * Hq}, "
+            "cpu_model": cpu_model(), "sample": f"{rows.size} seeded (sequence, query, q head) rows of {S * Q * Hq}, "
                       f"{reps} repetition(s), fp64 C oracle with OpenMP"}
 
 
@@ -196,9 +316,24 @@ def main():
     bps = args.blocks_per_split
     ws = torch.zeros(pda.pda_workspace_bytes(dims, bps) // 4, dtype=torch.float32, device=dev)
     out = torch.empty(w.num_seqs, w.num_q_heads, w.head_dim, dtype=torch.int16, device=dev)
-    kp, vp = pool.data_ptr() + 2 * w.k_base, pool.data_ptr() + 2 * w.v_base
     stream = torch.cuda.current_stream()
     S = w.num_seqs
+
+    # Pool copies rotated one per step, so that a pool that fits in the
+    # last-level cache (256 MB) is still read from HBM every step.
+    pool_bytes = pool.numel() * 2
+    ncopy = args.rotate
+    if ncopy < 0:
+        ncopy = max(7, -(-(1 << 30) // pool_bytes)) if (pool_bytes < (256 << 20) and w.name != "tiny") else 1
+    ncopy = max(1, ncopy)
+    pools = [pool] + [pool.clone() for _ in range(ncopy - 1)]
+    bases = [(p.data_ptr() + 2 * w.k_base, p.data_ptr() + 2 * w.v_base) for p in pools]
+    turn = [0]
+
+    def kv():
+        kp_, vp_ = bases[turn[0] % ncopy]
+        turn[0] += 1
+        return kp_, vp_
 
     if T == 1 and args.mask_drop is not None:
         api = f"pda_decode_masked (keep-mask dropping {args.mask_drop:.0%} of positions)"
@@ -207,6 +342,7 @@ def main():
         kv_mask = torch.from_numpy((mrng.random((S, width)) >= args.mask_drop).astype(np.uint8)).to(dev)
 
         def step():
+            kp, vp = kv()
             pda.pda_decode_masked(dims, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
                                   w.strides, kv_mask, width, ws, out, bps, stream)
     elif T == 1 and args.decode_via_prefill:
@@ -215,6 +351,7 @@ def main():
         pws = torch.empty(max(1, (pws_n + 3) // 4), dtype=torch.float32, device=dev) if pws_n else None
 
         def step():
+            kp, vp = kv()
             pda.pda_prefill(dims, 1, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
                             w.strides, True, None, 0, 0, pws, out, bps, 0, stream,
                             workspace_bytes=pws_n)
@@ -222,19 +359,13 @@ def main():
         api = "pda_decode"
 
         def step():
+            kp, vp = kv()
             pda.pda_decode(dims, q, kp, vp, tables[0], counts[0], lastv[0], w.block_size, S,
                            w.strides, ws, out, bps, stream)
     else:
         api = f"pda_begin_step + {T} x pda_step_tile + pda_finalize"
         state = torch.empty(pda.pda_state_bytes(dims) // 4, dtype=torch.float32, device=dev)
         plan = pda.pda_create(dims, state, ws, bps)
-
-        def step():
-            pda.pda_begin_step(plan, S, stream)
-            for t in range(T):
-                pda.pda_step_tile(plan, q, kp, vp, tables[t], counts[t], lastv[t], w.block_size,
-                                  S, w.strides, stream)
-            pda.pda_finalize(plan, out, S, stream)
 
     # Per-launch events around the attention kernel (armed before every call
     # that launches it), created once and recorded once so that they exist.
@@ -257,34 +388,20 @@ def main():
             step()
     else:
         def step_timed():
+            kp, vp = kv()
             pda.pda_begin_step(plan, S, stream)
             for t in range(T):
                 arm()
                 pda.pda_step_tile(plan, q, kp, vp, tables[t], counts[t], lastv[t], w.block_size,
                                   S, w.strides, stream)
             pda.pda_finalize(plan, out, S, stream)
+        step = step_timed   # arm() does nothing while no events are armed
 
-    log("warmup")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    m = measure(args, torch, stream, step)
     if n_ev:
-        # the same steps again, with every attention launch bracketed by its
-        # own event pair (recording them costs a few microseconds per step,
-        # so they stay out of the region above)
+        # K more steps, with every attention launch bracketed by its own event
+        # pair (recording them costs a few microseconds per step, so they stay
+        # out of the regions above)
         log(f"timing {args.steps} steps with per-launch attention-kernel events")
         arm_iter[0] = iter(range(n_ev))
         for _ in range(args.steps):
@@ -292,6 +409,7 @@ def main():
         torch.cuda.synchronize()
         arm_iter[0] = None
     nbytes = w.algorithmic_bytes()
+    ms = m["wall_us"] / 1e3
     tbs = nbytes / (ms * 1e-3) / 1e12
     kernel_us = None
     if n_ev:
@@ -303,7 +421,7 @@ def main():
         kernel_desc = ("prefill_kernel at q_len 1" if args.decode_via_prefill else
                        "attend_kernel (paged split-KV attention)") + ", average over the timed launches"
     else:
-        achieved_gbs = nbytes / (ev_ms * 1e-3) / 1e9
+        achieved_gbs = nbytes / (m["event_us"] * 1e-6) / 1e9
         kernel_desc = f"{api} step (all launches)"
     traffic = committed_traffic(w.name) if (kernel_us and args.mask_drop is None
                                             and not args.decode_via_prefill) else None
@@ -327,14 +445,15 @@ def main():
                    "block_size": w.block_size, "total_tokens": w.total_tokens,
                    "algorithmic_bytes": nbytes, "layout": w.layout, "api": api,
                    "blocks_per_split": bps if args.decode_via_prefill else pda.pda_blocks_per_split(dims, bps),
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": kernel_desc,
-                     "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": int(bytes_per_launch),
-                     "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
-                     "launches_per_step": launches},
+                   "pool_copies_rotated": ncopy, "parallelism": "single GPU"},
     }
+    res.update(steady_fields(m, nbytes, "TB/s", 1e12))
+    res["roofline"] = {"bound": "hbm", "kernel": kernel_desc,
+                       "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                       "algorithmic_bytes_per_launch": int(bytes_per_launch),
+                       "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
+                       "launches_per_step": launches}
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
@@ -365,16 +484,8 @@ def main_prefill(args, w, torch, pda, dev):
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in ev_b + ev_a:
         e.record(stream)
-    log("warmup")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    m = measure(args, torch, stream, step)
+    ms = m["wall_us"] / 1e3
     kernel_us = None
     if n_ev:
         log(f"timing {args.steps} steps with per-launch attention-kernel events")
@@ -416,6 +527,7 @@ def main_prefill(args, w, torch, pda, dev):
                      "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
                      "launches_per_step": 1},
     }
+    res.update(steady_fields(m, flops, "TFLOP/s", 1e12))
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle, sampled rows)")
         res["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
@@ -455,14 +567,8 @@ def main_rope(args, w, torch, pda, dev):
         pda.pda_rope_append_kv(dims, kv[0], kv[1], T, sqd, pd, cd, sd, P, table, kp, vp, w.strides,
                                stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    m = measure(args, torch, stream, step)
+    ms = m["wall_us"] / 1e3
     # the rope kernel alone (one launch per pda_rope call), events on its stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
@@ -495,6 +601,7 @@ def main_rope(args, w, torch, pda, dev):
                      "algorithmic_bytes_per_launch": q_bytes,
                      "kernel_us_per_launch": round(rope_us, 2), "launches_per_step": 2},
     }
+    res.update(steady_fields(m, nbytes, "TB/s", 1e12))
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
         reps, t0 = 0, time.perf_counter()
@@ -505,7 +612,7 @@ def main_rope(args, w, torch, pda, dev):
             if el >= args.cpu_seconds:
                 break
         res["cpu_baseline"] = {"value": q_bytes / (el / reps) / 1e12, "unit": "TB/s", "cores": 1,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"q rows of the whole step ({T} tokens x {Hq} heads), "
                                          f"{reps} repetition(s), fp64 C oracle, one thread"}
     print(json.dumps(res), flush=True)
