@@ -28,7 +28,9 @@
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device memory owned by the caller; the
  *    library never allocates, frees or retains device memory and keeps no
- *    global device state.  pda_plan is a small host-side handle.
+ *    global device state, except the fixed scratch array of
+ *    pda_decode_noalloc (PDA_NOALLOC_SCRATCH_BYTES per GPU, part of the
+ *    library's code object).  pda_plan is a small host-side handle.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued on it and the call returns without synchronising; a device
  *    fault therefore surfaces at the caller's next synchronisation.
@@ -190,6 +192,37 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
                       const int32_t *last_block_valid, int32_t last_block_valid_default,
                       int32_t num_seqs, pda_strides strides, void *workspace,
                       size_t workspace_bytes, void *out, int32_t blocks_per_split, void *stream);
+
+/* Bytes of the scratch array built into the library for pda_decode_noalloc
+ * (one array per GPU, from the library's load until the process ends). */
+#define PDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* pda_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: the split partials and control words live in a scratch
+ * array with static storage inside the library, PDA_NOALLOC_SCRATCH_BYTES on
+ * each GPU, whose device address is looked up once per device (on the first
+ * call with that device current).  The call allocates nothing and calls no
+ * allocating routine; q, the pools, the tables and `out` are the caller's.
+ * Arguments, results and errors as pda_decode, with the scratch in place of
+ * `workspace`; the current device must be the one `stream` belongs to.
+ *   PDA_ERR_WORKSPACE  if these dims and blocks_per_split need more than
+ *                      PDA_NOALLOC_SCRATCH_BYTES (pda_workspace_bytes(dims,
+ *                      blocks_per_split) > the limit); raise
+ *                      blocks_per_split, lower max_seqs / tile_capacity or
+ *                      call pda_decode with a workspace
+ *   PDA_ERR_HIP        if the scratch address cannot be looked up
+ * Every call on a GPU shares that GPU's scratch and keeps the last call's
+ * contents there; each call clears the control words it needs on `stream`
+ * before its kernels run.  Calls that overlap on one GPU (different streams
+ * or threads without ordering) race on the scratch and give wrong results:
+ * order them, for example on one stream. */
+pda_status pda_decode_noalloc(const pda_dims *dims, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *block_tables,
+                              const int32_t *block_counts, const int32_t *last_block_valid,
+                              int32_t last_block_valid_default, int32_t num_seqs,
+                              pda_strides strides, void *out, int32_t blocks_per_split,
+                              void *stream);
 
 /* pda_decode with a boolean keep-mask over each sequence's kv positions
  * ([CK] Python Wrappers: mask [batch, kv_len], true = keep).

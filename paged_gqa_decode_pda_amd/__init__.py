@@ -41,7 +41,7 @@ for _i, _n in enumerate(STATUS_NAMES):
 EXPORTED = ["pda_dims_validate", "pda_state_bytes", "pda_state_offsets", "pda_blocks_per_split",
             "pda_workspace_bytes", "pda_paged_strides", "pda_scratch_pool_strides",
             "pda_scratch_pool_v_offset", "pda_create", "pda_destroy", "pda_begin_step",
-            "pda_step_tile", "pda_finalize", "pda_decode", "pda_decode_masked",
+            "pda_step_tile", "pda_finalize", "pda_decode", "pda_decode_noalloc", "pda_decode_masked",
             "pda_prefill_workspace_bytes", "pda_prefill", "pda_rope", "pda_rope_append_kv",
             "pda_debug_time_attention",
             "pda_status_string", "pda_last_error"]
@@ -94,6 +94,8 @@ _sig("pda_step_tile", ctypes.c_int, _P, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_
 _sig("pda_finalize", ctypes.c_int, _P, _P, _i32, _P)
 _sig("pda_decode", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P, _sz,
      _P, _i32, _P)
+_sig("pda_decode_noalloc", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P,
+     _i32, _P)
 _sig("pda_decode_masked", ctypes.c_int, _PD, _P, _P, _P, _P, _P, _P, _i32, _i32, pda_strides, _P,
      _i64, _P, _sz, _P, _i32, _P)
 _sig("pda_prefill_workspace_bytes", _sz, _PD, _i32, _i32)
@@ -254,6 +256,23 @@ def pda_decode(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_v
                            _addr(block_tables), _addr(block_counts), _addr(last_block_valid),
                            last_block_valid_default, num_seqs, _strides(strides), _addr(workspace),
                            nb, _addr(out), blocks_per_split, _stream(stream)))
+
+
+# Bytes of the library's built-in scratch for pda_decode_noalloc (per GPU).
+PDA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pda_decode_noalloc(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                       last_block_valid_default: int, num_seqs: int, strides, out,
+                       blocks_per_split: int = 0, stream=None) -> None:
+    """pda_decode with the library's built-in scratch instead of a workspace:
+    allocates nothing (for callers that cannot allocate device memory)."""
+    d = _dims(dims)
+    _check(_lib.pda_decode_noalloc(ctypes.byref(d), _addr(q), _addr(k_pool), _addr(v_pool),
+                                   _addr(block_tables), _addr(block_counts),
+                                   _addr(last_block_valid), last_block_valid_default, num_seqs,
+                                   _strides(strides), _addr(out), blocks_per_split,
+                                   _stream(stream)))
 
 
 def pda_decode_masked(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/pda.h: argument validation, split
 // planning and kernel launches.  Nothing here allocates device memory or
-// synchronises; every check runs before the first enqueue.
+// synchronises (the one device array, pda_decode_noalloc's scratch, has
+// static storage); every check runs before the first enqueue.
 #include "../../include/pda.h"
 
 #include <hip/hip_runtime.h>
@@ -10,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "pda_internal.h"
@@ -188,6 +190,39 @@ pda_status hip_fail(hipError_t e, const char *what) {
     return fail(PDA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The workspace of pda_decode_noalloc: a device array with static storage,
+// one copy per GPU the library runs on (created with the code object on that
+// device, zero at load, held until the process ends).  Host code never uses
+// the array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address is looked up once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[PDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+pda_status noalloc_scratch(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PDA_ERR_DIMS, "device %d is beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(PDA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return PDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,7 +378,7 @@ pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, 
                        const int32_t *last_block_valid, int32_t last_block_valid_default,
                        int32_t num_seqs, pda_strides strides, const uint8_t *kv_mask,
                        int64_t mask_stride, void *workspace, size_t workspace_bytes, void *out,
-                       int32_t blocks_per_split, void *stream) {
+                       int32_t blocks_per_split, void *stream, bool noalloc = false) {
     pda_status st = check_dims(dims);
     if (st != PDA_OK) return st;
     if (num_seqs < 0 || num_seqs > dims->max_seqs)
@@ -356,9 +391,19 @@ pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, 
     if ((st = check_strides(dims, strides)) != PDA_OK) return st;
     if (workspace && !aligned(workspace, 16))
         return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    if (num_seqs == 0) return PDA_OK;
     const int32_t bps = resolve_bps(dims, blocks_per_split, num_seqs);
     const size_t need = workspace_for(dims, bps);
+    if (noalloc && need > PDA_NOALLOC_SCRATCH_BYTES)
+        return fail(PDA_ERR_WORKSPACE,
+                    "pda_decode_noalloc needs %zu bytes of scratch for these dims and %d pages per "
+                    "split; its built-in scratch holds %zu (raise blocks_per_split, lower max_seqs "
+                    "or tile_capacity, or call pda_decode with a workspace)",
+                    need, bps, (size_t)PDA_NOALLOC_SCRATCH_BYTES);
+    if (num_seqs == 0) return PDA_OK;
+    if (noalloc) {
+        if ((st = noalloc_scratch(&workspace)) != PDA_OK) return st;
+        workspace_bytes = PDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < need)
         return fail(PDA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
     const int G = dims->num_q_heads / dims->num_kv_heads;
@@ -369,6 +414,12 @@ pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, 
     a.out = static_cast<uint16_t *>(out);
     a.mask = kv_mask;
     a.mask_stride = mask_stride;
+    if (noalloc) {
+        // the shared scratch keeps the last call's contents: its control
+        // words are cleared here, on the call's stream, before the kernels
+        hipError_t z = pda::launch_zero_ints(a.ctrl, pda::kCtrlInts, static_cast<hipStream_t>(stream));
+        if (z != hipSuccess) return hip_fail(z, "scratch clear launch");
+    }
     hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "decode launch");
 }
@@ -384,6 +435,18 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
     return decode_impl(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
                        last_block_valid_default, num_seqs, strides, nullptr, 0, workspace,
                        workspace_bytes, out, blocks_per_split, stream);
+}
+
+pda_status pda_decode_noalloc(const pda_dims *dims, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *block_tables,
+                              const int32_t *block_counts, const int32_t *last_block_valid,
+                              int32_t last_block_valid_default, int32_t num_seqs,
+                              pda_strides strides, void *out, int32_t blocks_per_split,
+                              void *stream) {
+    clear_err();
+    return decode_impl(dims, q, k_pool, v_pool, block_tables, block_counts, last_block_valid,
+                       last_block_valid_default, num_seqs, strides, nullptr, 0, nullptr, 0, out,
+                       blocks_per_split, stream, true);
 }
 
 pda_status pda_decode_masked(const pda_dims *dims, const void *q, const void *k_pool,

@@ -112,5 +112,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int dp, int rb, hipStream_t st, 
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st);
 hipError_t launch_finalize(const float *l, const float *o, uint16_t *out, int64_t rows, int D,
                            hipStream_t st);
+// Fills n int32 with zero (a kernel, not a memset: safe inside captured graphs).
+hipError_t launch_zero_ints(int32_t *p, int64_t n, hipStream_t st);
 
 }  // namespace pda

@@ -923,6 +923,11 @@ __global__ void __launch_bounds__(256) reset_kernel(float *m, float *l, float *o
     }
 }
 
+__global__ void __launch_bounds__(256) zero_ints_kernel(int32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 __global__ void __launch_bounds__(256) finalize_kernel(const float *l, const float *o, uint16_t *out,
                                                        int64_t rows, int D) {
     const int64_t n = rows * D;
@@ -1019,6 +1024,11 @@ hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_
 
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st) {
     hipLaunchKernelGGL(reset_kernel, dim3(grid_1d(rows * D, 256)), dim3(256), 0, st, m, l, o, rows, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_ints(int32_t *p, int64_t n, hipStream_t st) {
+    hipLaunchKernelGGL(zero_ints_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

@@ -364,3 +364,41 @@ def test_rope_validation_before_enqueue():
             pda.pda_rope_append_kv(**{**app, **change})
         assert e.value.status == status, (change, e.value)
     pda.pda_rope_append_kv(**{**app, "num_tokens": 0})
+
+
+def test_decode_noalloc_validation_before_enqueue():
+    d = dims()
+    st = (16 * 2 * 64, 2 * 64, 64)
+    args = dict(dims=d, q=FAKE, k_pool=FAKE, v_pool=FAKE, block_tables=FAKE, block_counts=FAKE,
+                last_block_valid=None, last_block_valid_default=16, num_seqs=4, strides=st,
+                out=FAKE, blocks_per_split=0, stream=0)
+    cases = [
+        (dict(q=None), pda.PDA_ERR_NULL),
+        (dict(out=None), pda.PDA_ERR_NULL),
+        (dict(out=FAKE + 4), pda.PDA_ERR_ALIGN),
+        (dict(num_seqs=5), pda.PDA_ERR_MAX_SEQS),
+        (dict(blocks_per_split=-1), pda.PDA_ERR_DIMS),
+        (dict(dims=dims(num_q_heads=6, num_kv_heads=4)), pda.PDA_ERR_GQA),
+    ]
+    for change, status in cases:
+        with pytest.raises(pda.PdaError) as e:
+            pda.pda_decode_noalloc(**{**args, **change})
+        assert e.value.status == status, (change, e.value)
+    # sizes whose partials exceed the built-in scratch are refused with the limit named
+    big = dims(max_seqs=4096, tile_capacity=4096)
+    need = pda.pda_workspace_bytes(big, 0)
+    assert need > pda.PDA_NOALLOC_SCRATCH_BYTES
+    with pytest.raises(pda.PdaError) as e:
+        pda.pda_decode_noalloc(**{**args, "dims": big})
+    assert e.value.status == pda.PDA_ERR_WORKSPACE
+    assert str(pda.PDA_NOALLOC_SCRATCH_BYTES) in str(e.value)
+    # a larger split fits; num_seqs == 0 is a no-op that needs no device
+    assert pda.pda_workspace_bytes(big, 4096) <= pda.PDA_NOALLOC_SCRATCH_BYTES
+    pda.pda_decode_noalloc(**{**args, "dims": big, "blocks_per_split": 4096, "num_seqs": 0})
+    pda.pda_decode_noalloc(**{**args, "num_seqs": 0})
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pda.PDA_NOALLOC_SCRATCH_BYTES
