@@ -210,7 +210,7 @@ def steady_fields(m, per_step_amount, unit, scale):
 # The sources each kernel's code and launch come from (a committed counter
 # summary holds for the kernel only while these hash to its recorded value).
 KERNEL_SOURCES = {
-    "attend_kernel": ["pda_device.h", "pda_internal.h", "pda_kernels.hip"],
+    "attend_kernel": ["pda_device.h", "pda_internal.h", "pda_attend.hip"],
     "prefill_kernel": ["pda_device.h", "pda_internal.h", "pda_prefill.hip"],
     "rope_kernel": ["pda_device.h", "pda_rope.h", "pda_rope.hip"],
 }

@@ -99,7 +99,8 @@ pda_status pda_dims_validate(const pda_dims *dims);
 
 /* Bytes of the fp32 running state ([TA] m_bytes + l_bytes + o_bytes): m and l
  * are [max_seqs, num_q_heads], o is [max_seqs, num_q_heads, head_dim], stored
- * back to back in that order in one caller-owned device buffer.  m is in
+ * in that order in one caller-owned device buffer, each starting on a 16-byte
+ * boundary (m and l padded up to a multiple of 16 bytes; pda_state_offsets).  m is in
  * natural-log units (the running max of the scaled scores), l the running sum
  * of exp(score - m), o the running sum of exp(score - m) * V.  0 if dims are
  * invalid. */
@@ -115,16 +116,18 @@ int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
 
 /* Device workspace bytes for max_seqs sequences with the given
  * blocks_per_split (0 = the library's choice, sized for any device): 256 bytes
- * of control words (work counters, then the work-item sizing one launch
- * passes from its attention kernel to its merge kernel) followed by the fp32
- * split partials, max_seqs * num_q_heads * slots * (head_dim + 2) * 4, where
- * slots = ceil(tile_capacity / bps), one per split (the kernel may group
- * splits into larger work items, which then share a slot).
- * The workspace must be zero-filled before its first use; every call that
- * completes leaves the work counters (the first two control words) zero
- * again, so a workspace is reused without clearing.  Calls that share a
- * workspace must not run concurrently (order them on one stream).  0 if dims
- * are invalid. */
+ * of control words (the work-item counter), one 64-bit arrival counter per
+ * (sequence, kv head, chunk of 16 q heads) padded to a multiple of 16 bytes,
+ * then the fp32 split partials: the (m, l) pairs, rows * slots * 2 * 4 bytes
+ * padded up to a multiple of 16, then the o rows, rows * slots * head_dim * 4,
+ * where rows = max_seqs * num_q_heads and slots = ceil(tile_capacity / bps),
+ * one per split (the kernel may group splits into larger work items, which
+ * then share a slot).
+ * The workspace needs no clearing, before its first use or ever: every
+ * counter is tagged with the launch that counts in it, and a launch restarts
+ * any counter another launch (or leftover content) left behind.  Calls that
+ * share a workspace must not run concurrently (order them on one stream).  0
+ * if dims are invalid. */
 size_t pda_workspace_bytes(const pda_dims *dims, int32_t blocks_per_split);
 
 /* ([TA] paged_strides) layout [num_blocks, block_size, num_kv_heads, head_dim]:
@@ -141,8 +144,7 @@ int64_t pda_scratch_pool_v_offset(const pda_dims *dims);
 /* Creates a plan over caller-owned device buffers ([TA] TiledAttention::new,
  * which allocates its own state; here the caller does):
  *   state      device, pda_state_bytes(dims) bytes
- *   workspace  device, at least pda_workspace_bytes(dims, blocks_per_split),
- *              zero-filled before its first use
+ *   workspace  device, at least pda_workspace_bytes(dims, blocks_per_split)
  *   blocks_per_split  0 = the library's choice
  * The buffers must outlive the plan.  *out receives the handle. */
 pda_status pda_create(const pda_dims *dims, void *state, void *workspace, size_t workspace_bytes,
@@ -183,8 +185,7 @@ pda_status pda_finalize(pda_plan *plan, void *out, int32_t num_seqs, void *strea
  * split-KV).
  * Arguments as pda_step_tile plus:
  *   dims        as for pda_create (num_seqs <= dims->max_seqs)
- *   workspace   device, at least pda_workspace_bytes(dims, blocks_per_split),
- *               zero-filled before its first use
+ *   workspace   device, at least pda_workspace_bytes(dims, blocks_per_split)
  *   out         device bf16 [num_seqs, num_q_heads, head_dim]
  * A sequence with no token gets an all-zero output row. */
 pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, const void *v_pool,
@@ -213,10 +214,10 @@ pda_status pda_decode(const pda_dims *dims, const void *q, const void *k_pool, c
  *                      call pda_decode with a workspace
  *   PDA_ERR_HIP        if the scratch address cannot be looked up
  * Every call on a GPU shares that GPU's scratch and keeps the last call's
- * contents there; each call clears the control words it needs on `stream`
- * before its kernels run.  Calls that overlap on one GPU (different streams
- * or threads without ordering) race on the scratch and give wrong results:
- * order them, for example on one stream. */
+ * contents there; nothing in it needs clearing (its counters are tagged with
+ * the launch that counts in them, as in any workspace).  Calls that overlap on
+ * one GPU (different streams or threads without ordering) race on the scratch
+ * and give wrong results: order them, for example on one stream. */
 pda_status pda_decode_noalloc(const pda_dims *dims, const void *q, const void *k_pool,
                               const void *v_pool, const int32_t *block_tables,
                               const int32_t *block_counts, const int32_t *last_block_valid,

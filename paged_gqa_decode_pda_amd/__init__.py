@@ -344,10 +344,33 @@ def apply_rotary_emb(x, freqs_cis, positions, out=None, stream=None):
     pos = positions.to(device=x.device, dtype=torch.int32).contiguous()
     if pos.numel() != B * L:
         raise ValueError("positions must hold one entry per token")
+    own = []
     if out is None:
         out = torch.empty_like(x)
-    pda_rope(x, out, B * L, H, D, cos_t.contiguous(), sin_t.contiguous(), cos_t.shape[0], pos, stream)
+        own.append(out)
+    ct, st = cos_t.contiguous(), sin_t.contiguous()
+    _use_on_stream(stream, [pos, ct, st] + own)
+    pda_rope(x, out, B * L, H, D, ct, st, cos_t.shape[0], pos, stream)
     return out
+
+
+def _use_on_stream(stream, temporaries):
+    """Ordering for a wrapper that computes temporaries with torch ops (on
+    torch's current stream) and launches on another stream: that stream
+    first waits for the work enqueued so far on the current one, and every
+    temporary is marked as used on it, so torch's caching allocator does not
+    hand its memory out again before that stream is done with it.  A raw
+    integer stream handle carries no such information: the caller orders it."""
+    import torch
+    if stream is None or isinstance(stream, int):
+        return
+    cur = torch.cuda.current_stream(stream.device)
+    if stream == cur:
+        return
+    stream.wait_stream(cur)
+    for t in temporaries:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _paged_args(q, k_cache, v_cache, block_table, seq_lens):
@@ -393,11 +416,14 @@ def attn_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, is_causal: bo
         raise ValueError("mask rows are shorter than the longest sequence")
     dims, strides, block_table, counts, lastv = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
     bs = dims.block_size
+    own = []
     if out is None:
         out = torch.empty((B, Q, Hq, D), dtype=torch.bfloat16, device=q.device)
+        own.append(out)
     if workspace is None:
         nb = pda_prefill_workspace_bytes(dims, Q, blocks_per_split)
         workspace = torch.empty(max(1, (nb + 3) // 4), dtype=torch.float32, device=q.device)
+        own.append(workspace)
     m, ss, qs = None, 0, 0
     if mask is not None:
         m = mask.to(device=q.device, dtype=torch.uint8).contiguous()
@@ -407,6 +433,7 @@ def attn_paged_prefill(q, k_cache, v_cache, block_table, seq_lens, is_causal: bo
             ss, qs = m.shape[1] * m.shape[2], m.shape[2]
         else:
             raise ValueError("mask must be [batch, kv_len] or [batch, q_len, kv_len]")
+    _use_on_stream(stream, [block_table, counts, lastv, m] + own)
     pda_prefill(dims, Q, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
                 is_causal, m, ss, qs, workspace, out, blocks_per_split, rows_per_wave, stream)
     return out
@@ -433,18 +460,24 @@ def attn_paged_decode(q, k_cache, v_cache, block_table, seq_lens, mask=None, out
         raise ValueError("mask rows are shorter than the longest sequence")
     dims, strides, block_table, counts, lastv = _paged_args(q, k_cache, v_cache, block_table, seq_lens)
     bs = dims.block_size
+    own = []
     if out is None:
         out = torch.empty((B, 1, Hq, D), dtype=torch.bfloat16, device=q.device)
-    if workspace is None:
-        workspace = torch.zeros(max(1, pda_workspace_bytes(dims, blocks_per_split) // 4),
+        own.append(out)
+    if workspace is None:   # needs no clearing
+        workspace = torch.empty(max(1, pda_workspace_bytes(dims, blocks_per_split) // 4),
                                 dtype=torch.float32, device=q.device)
-    if mask is None:
-        pda_decode(dims, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
-                   workspace, out, blocks_per_split, stream)
-    else:
+        own.append(workspace)
+    m = None
+    if mask is not None:
         m = mask.to(device=q.device, dtype=torch.uint8).contiguous()
         if m.dim() != 2 or m.shape[0] != B:
             raise ValueError("mask must be [batch, kv_len]")
+    _use_on_stream(stream, [block_table, counts, lastv, m] + own)
+    if m is None:
+        pda_decode(dims, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
+                   workspace, out, blocks_per_split, stream)
+    else:
         pda_decode_masked(dims, q, k_cache, v_cache, block_table, counts, lastv, bs, B, strides,
                           m, m.shape[1], workspace, out, blocks_per_split, stream)
     return out

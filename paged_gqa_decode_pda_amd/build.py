@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_PATH = os.path.join(HERE, "libpda.so")
-SOURCES = [os.path.join(HERE, "csrc", n) for n in ("pda_api.hip", "pda_kernels.hip", "pda_prefill.hip", "pda_rope.hip")]
+SOURCES = [os.path.join(HERE, "csrc", n) for n in ("pda_api.hip", "pda_kernels.hip", "pda_attend.hip", "pda_prefill.hip",
+                                                  "pda_rope.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are disabled for every HIP translation unit; hipcc's

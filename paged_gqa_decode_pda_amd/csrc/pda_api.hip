@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -42,6 +44,10 @@ void clear_err() { g_err[0] = 0; }
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bytes rounded up to a multiple of 16 (the start of every region the
+// kernels read or write with 16-byte accesses).
+size_t round16(size_t n) { return (n + 15) & ~size_t(15); }
 
 pda_status check_dims(const pda_dims *d) {
     if (!d) return fail(PDA_ERR_NULL, "dims is NULL");
@@ -114,14 +120,42 @@ int64_t units_of(const pda_dims *d) {
     return (int64_t)d->num_kv_heads * pda::choose_plan(G, d->head_dim, d->block_size).nhc;
 }
 
-// Control words (int32), then split partials for max_seqs sequences:
-// (m, l) pairs, then o rows.
-size_t control_ints(const pda_dims *) { return (size_t)pda::kCtrlInts; }
+// The decode workspace: control words, the arrival counters (one 64-bit word
+// per (sequence, unit)), then the split partials for max_seqs sequences:
+// (m, l) pairs, padded to 16 bytes, then o rows.
+size_t arrive_bytes(const pda_dims *d) { return round16((size_t)d->max_seqs * units_of(d) * 8); }
+
+// (m, l) pairs of the partials, in floats, padded to 16 bytes so the o rows
+// after them start 16-byte aligned.
+size_t partial_ml_floats(const pda_dims *d, int32_t bps) {
+    return round16((size_t)d->max_seqs * d->num_q_heads * slots_per_seq(d, bps) * 2 * sizeof(float)) /
+           sizeof(float);
+}
+
+// A unit's partial o rows (its q heads, every split slot) must span less than
+// 2 GiB: the kernel addresses them with 32-bit offsets from the unit's start.
+pda_status check_partial_span(const pda_dims *d, int32_t bps) {
+    const int G = d->num_q_heads / d->num_kv_heads;
+    const int64_t heads = G < pda::kHeadsPerItem ? G : pda::kHeadsPerItem;
+    if (heads * slots_per_seq(d, bps) * d->head_dim * 4 >= (int64_t(1) << 31))
+        return fail(PDA_ERR_DIMS, "%lld split slots per sequence (tile_capacity / blocks_per_split) are too many",
+                    (long long)slots_per_seq(d, bps));
+    return PDA_OK;
+}
 
 size_t workspace_for(const pda_dims *d, int32_t bps) {
-    return control_ints(d) * sizeof(int32_t) +
-           (size_t)d->max_seqs * d->num_q_heads * slots_per_seq(d, bps) * (d->head_dim + 2) * sizeof(float);
+    return (size_t)pda::kCtrlBytes + arrive_bytes(d) + partial_ml_floats(d, bps) * sizeof(float) +
+           (size_t)d->max_seqs * d->num_q_heads * slots_per_seq(d, bps) * d->head_dim * sizeof(float);
 }
+
+// Launch epochs: each attention launch tags the workspace counters with its
+// own 32-bit value.  The sequence starts at a value drawn from the clock when
+// the library is loaded, so launches of this process do not meet epochs that a
+// previous user of the same memory left behind (other than by a 2^-32 chance).
+std::atomic<uint32_t> g_epoch{(uint32_t)(std::chrono::steady_clock::now().time_since_epoch().count() *
+                                         0x9E3779B97F4A7C15ull >> 32)};
+
+uint32_t next_epoch() { return g_epoch.fetch_add(1, std::memory_order_relaxed) + 1; }
 
 pda_status check_strides(const pda_dims *d, pda_strides st) {
     if (st.blk < 0 || st.tok < 0 || st.kvh < 0)
@@ -173,12 +207,14 @@ pda::AttendArgs attend_args(const pda_dims *d, const void *q, const void *k, con
     a.nsplit = (int32_t)slots_per_seq(d, bps);   // partial slots per (sequence, q head)
     a.lv_default = lv_default;
     a.prefix_mode = S <= pda::kPrefixMaxSeqs ? 1 : 0;
+    a.epoch = next_epoch();
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
-    int32_t *wsi = static_cast<int32_t *>(ws);
-    a.ctrl = wsi;
-    float *wsf = reinterpret_cast<float *>(wsi + control_ints(d));
+    char *wsb = static_cast<char *>(ws);
+    a.work = reinterpret_cast<unsigned long long *>(wsb);
+    a.arrive = reinterpret_cast<unsigned long long *>(wsb + pda::kCtrlBytes);
+    float *wsf = reinterpret_cast<float *>(wsb + pda::kCtrlBytes + arrive_bytes(d));
     a.part_ml = wsf;
-    a.part_o = wsf + (int64_t)d->max_seqs * d->num_q_heads * a.nsplit * 2;
+    a.part_o = wsf + partial_ml_floats(d, bps);
     a.out = nullptr;
     a.m = a.l = a.o = nullptr;
     a.mask = nullptr;
@@ -235,7 +271,7 @@ pda_status pda_dims_validate(const pda_dims *dims) {
 size_t pda_state_bytes(const pda_dims *d) {
     if (check_dims(d) != PDA_OK) return 0;
     const size_t rows = (size_t)d->max_seqs * d->num_q_heads;
-    return rows * sizeof(float) * (2 + (size_t)d->head_dim);
+    return 2 * round16(rows * sizeof(float)) + rows * sizeof(float) * (size_t)d->head_dim;
 }
 
 pda_status pda_state_offsets(const pda_dims *d, size_t offsets[3]) {
@@ -245,8 +281,8 @@ pda_status pda_state_offsets(const pda_dims *d, size_t offsets[3]) {
     if (!offsets) return fail(PDA_ERR_NULL, "offsets is NULL");
     const size_t rows = (size_t)d->max_seqs * d->num_q_heads;
     offsets[0] = 0;
-    offsets[1] = rows * sizeof(float);
-    offsets[2] = 2 * rows * sizeof(float);
+    offsets[1] = round16(rows * sizeof(float));
+    offsets[2] = 2 * round16(rows * sizeof(float));
     return PDA_OK;
 }
 
@@ -303,9 +339,10 @@ pda_status pda_create(const pda_dims *dims, void *state, void *workspace, size_t
     if (!p) return fail(PDA_ERR_DIMS, "out of host memory");
     p->dims = *dims;
     const size_t rows = (size_t)dims->max_seqs * dims->num_q_heads;
+    const size_t mlen = round16(rows * sizeof(float)) / sizeof(float);   // m and l, each padded to 16 bytes
     p->m = static_cast<float *>(state);
-    p->l = p->m + rows;
-    p->o = p->l + rows;
+    p->l = p->m + mlen;
+    p->o = p->l + mlen;
     p->workspace = workspace;
     p->workspace_bytes = workspace_bytes;
     p->bps_request = blocks_per_split;
@@ -342,6 +379,7 @@ pda_status pda_step_tile(pda_plan *plan, const void *q, const void *k_pool, cons
     if ((st = check_strides(d, strides)) != PDA_OK) return st;
     if (num_seqs == 0) return PDA_OK;
     const int32_t bps = resolve_bps(d, plan->bps_request, num_seqs);
+    if ((st = check_partial_span(d, bps)) != PDA_OK) return st;
     if (workspace_for(d, bps) > plan->workspace_bytes)
         return fail(PDA_ERR_WORKSPACE, "workspace too small");
     const int G = d->num_q_heads / d->num_kv_heads;
@@ -392,6 +430,7 @@ pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, 
     if (workspace && !aligned(workspace, 16))
         return fail(PDA_ERR_ALIGN, "workspace must be 16-byte aligned");
     const int32_t bps = resolve_bps(dims, blocks_per_split, num_seqs);
+    if ((st = check_partial_span(dims, bps)) != PDA_OK) return st;
     const size_t need = workspace_for(dims, bps);
     if (noalloc && need > PDA_NOALLOC_SCRATCH_BYTES)
         return fail(PDA_ERR_WORKSPACE,
@@ -414,12 +453,6 @@ pda_status decode_impl(const pda_dims *dims, const void *q, const void *k_pool, 
     a.out = static_cast<uint16_t *>(out);
     a.mask = kv_mask;
     a.mask_stride = mask_stride;
-    if (noalloc) {
-        // the shared scratch keeps the last call's contents: its control
-        // words are cleared here, on the call's stream, before the kernels
-        hipError_t z = pda::launch_zero_ints(a.ctrl, pda::kCtrlInts, static_cast<hipStream_t>(stream));
-        if (z != hipSuccess) return hip_fail(z, "scratch clear launch");
-    }
     hipError_t e = pda::launch_attend(p, a, device_cus(), static_cast<hipStream_t>(stream), take_events());
     return e == hipSuccess ? PDA_OK : hip_fail(e, "decode launch");
 }

@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host code (pda_api.hip) and the gfx950
-// kernels (pda_kernels.hip).  Not installed; not part of the ABI.
+// kernels (pda_attend.hip, pda_kernels.hip, pda_prefill.hip, pda_rope.hip).
+// Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,16 +8,19 @@
 
 namespace pda {
 
-// Layout of the caller's workspace, in this order:
-//   ctrl      64 int32: [0] next work item, [1] finished waves; [32..33]
-//             (the next 128-byte line) item sizing passed from the attention
-//             kernel to the merge kernel
-//   part_ml   fp32 [max_seqs, Hq, nsplit, 2]: (m in log2 units, l) per split
+// Layout of the caller's decode workspace, in this order:
+//   ctrl      256 bytes; ctrl[0] (64-bit) is the work-item counter
+//   arrive    uint64 [max_seqs, units]: per (sequence, kv head + head chunk),
+//             the number of its split items that have left their partials
+//   part_ml   fp32 [max_seqs, Hq, nsplit, 2]: (m in log2 units, l) per split,
+//             padded to a multiple of 16 bytes
 //   part_o    fp32 [max_seqs, Hq, nsplit, D]
-// ctrl[0..1] must be zero before a launch; every launch that completes leaves
-// them zero again.
-constexpr int kCtrlInts = 64;
-constexpr int kCtrlSizing = 32;
+// The counters are 64-bit words (epoch << 32 | count): the high half names
+// the launch that last counted in it (AttendArgs::epoch, unique per launch),
+// and the first claim of a launch that finds another launch's epoch (or any
+// leftover content) restarts the word at its own epoch.  So the workspace
+// needs no clearing, before its first use or after a failed launch.
+constexpr int kCtrlBytes = 256;
 
 // Everything the attention kernel needs, passed by value.
 struct AttendArgs {
@@ -26,7 +30,8 @@ struct AttendArgs {
     const int32_t *blocks;    // int32 [S, cap] page ids
     const int32_t *counts;    // int32 [S]
     const int32_t *lastv;     // int32 [S] or null
-    int32_t *ctrl;            // workspace control words
+    unsigned long long *work;     // workspace: the work-item counter
+    unsigned long long *arrive;   // workspace: arrival counters [S, units]
     float *part_ml;           // workspace partials
     float *part_o;
     uint16_t *out;            // bf16 [S, Hq, D] (decode) or null
@@ -37,37 +42,38 @@ struct AttendArgs {
     uint64_t bs_magic;        // ceil(2^32 / bs): t / bs == (t * bs_magic) >> 32 for t < 2^24
     int32_t S, Hq, Hkv, G, D, bs, cap, bps, nhc, nsplit, lv_default;
     int32_t prefix_mode;      // 1: enumerate only non-empty splits (needs 2 (S + 1) ints of LDS)
+    uint32_t epoch;           // this launch's counter epoch (never reused by a recent launch)
     float scale_log2;         // log2(e) / sqrt(D)
 };
 
 // Choices the host makes before launching.
 struct Plan {
     int dp;     // padded head dim: 64, 128 or 256
-    int gc;     // q heads per work item: 1, 2, 4 or 8
-    int nhc;    // head chunks per kv head: ceil(G / gc)
+    int nhc;    // head chunks per kv head: ceil(G / kHeadsPerItem)
     bool p16;   // block_size % 16 == 0: every 16-token group lies inside one page
 };
 
+// q heads of one kv head that a decode work item takes (the columns of the
+// matrix-core products).
+constexpr int kHeadsPerItem = 16;
+
 Plan choose_plan(int G, int D, int bs);
 
-// Sequences up to this count enumerate work items through an LDS prefix sum.
-constexpr int kPrefixMaxSeqs = 16384;
+// Sequences up to this count enumerate work items through LDS prefix sums
+// (3 (S + 1) ints next to the kernel's V tiles, up to 37 KB, within gfx950's
+// 160 KB of LDS per workgroup).
+constexpr int kPrefixMaxSeqs = 10240;
 
 // Work-item sizing with the prefix enumeration (decided in the attention
 // kernel from the total work): with at least kBigTokensLarge tokens of work
 // per wave, "big" items span kBigTokensLarge tokens (at least one split) and
 // take kEighthsLarge / 8 of a sequence's splits; with less, every split is an
-// item of its own when that makes no more items than waves, else
-// kEighthsPaired / 8 of the splits go in pairs.  The attention kernel leaves
-// its choice (splits per big item, eighths) in control words kCtrlSizing and
-// kCtrlSizing + 1 for the merge kernel.
+// item of its own when that makes no more items than waves (one round, equal
+// lengths), else kEighthsPaired / 8 of the splits go in pairs.
 constexpr int kBigTokensLarge = 1024;
 constexpr int kEighthsLarge = 7;
 constexpr int kEighthsPaired = 6;
 
-// Launches the persistent attention kernel and, when sequences may have
-// several splits, the combine kernel (decode when a.out is set, else a tile
-// folded into the running state).  `cus` is the device's compute-unit count.
 // Optional events recorded on the launch stream right before and right after
 // the attention kernel (timing diagnostics); null members are skipped.
 struct AttendEvents {
@@ -75,6 +81,9 @@ struct AttendEvents {
     hipEvent_t after = nullptr;
 };
 
+// Launches the persistent decode attention kernel (decode when a.out is set,
+// else a tile folded into the running state); the split merge runs inside it.
+// `cus` is the device's compute-unit count.
 hipError_t launch_attend(const Plan &p, const AttendArgs &a, int cus, hipStream_t st,
                          const AttendEvents &ev);
 
@@ -112,7 +121,6 @@ hipError_t launch_prefill(const PrefillArgs &a, int dp, int rb, hipStream_t st, 
 hipError_t launch_reset(float *m, float *l, float *o, int64_t rows, int D, hipStream_t st);
 hipError_t launch_finalize(const float *l, const float *o, uint16_t *out, int64_t rows, int D,
                            hipStream_t st);
-// Fills n int32 with zero (a kernel, not a memset: safe inside captured graphs).
-hipError_t launch_zero_ints(int32_t *p, int64_t n, hipStream_t st);
+
 
 }  // namespace pda

@@ -62,50 +62,11 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 values to a bf16 pair, round to nearest even (one
-// v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // The running max a row's weights are taken against moves only when the
 // row's true max exceeds it by more than this (log2 units): weights stay
 // below 2^kRescaleSlack, and the rescale of the accumulators is rare.
 constexpr float kRescaleSlack = 8.f;
 
-// x of lanes l and l^16 (gfx950 v_permlane16_swap of x with itself: the two
-// results hold, per lane, the values of lanes l & ~16 and l | 16), and the
-// same for l^32 (v_permlane32_swap).  VALU lane swaps, no LDS round trip.
-__device__ __forceinline__ void pair16(float x, float &a, float &b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void pair32(float x, float &a, float &b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-}
-
-// Maximum of x over the four lanes l, l^16, l^32, l^48 (one row of the
-// transposed scores).
-__device__ __forceinline__ float max4(float x) {
-    float a, b;
-    pair16(x, a, b);
-    pair32(fmaxf(a, b), a, b);
-    return fmaxf(a, b);
-}
-// Sum over the same four lanes, in an order that is the same in every lane
-// (lanes with bit 4 clear first, then bit 5 clear first).
-__device__ __forceinline__ float sum4(float x) {
-    float a, b;
-    pair16(x, a, b);
-    pair32(a + b, a, b);
-    return a + b;
-}
 __device__ __forceinline__ int wave_max_i(int x) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) x = max(x, __shfl_xor(x, m, 64));

@@ -93,8 +93,11 @@ class Device:
 
     def workspace(self, bps=0):
         n = self.pda.pda_workspace_bytes(self.dims(), bps)
-        # zero-filled before first use, as the library requires
-        return self.torch.zeros(max(1, n // 4), dtype=self.torch.float32, device=self.dev)
+        # the library needs no cleared workspace: start from all-ones bytes
+        # (NaN partials, counters holding no launch's epoch)
+        ws = self.torch.empty(max(1, n // 4), dtype=self.torch.int32, device=self.dev)
+        ws.fill_(-1)
+        return ws
 
     def new_out(self, fill=None):
         t = self.torch.empty(self.max_seqs, self.p.Hq, self.p.D, dtype=self.torch.int16,
@@ -152,8 +155,9 @@ class Device:
         """(m [max_seqs, Hq], l, o [max_seqs, Hq, D]) host fp32 views of a state buffer."""
         s = state.cpu().numpy()
         r = self.max_seqs * self.p.Hq
-        return s[:r].reshape(self.max_seqs, self.p.Hq), s[r:2 * r].reshape(self.max_seqs, self.p.Hq), \
-            s[2 * r:].reshape(self.max_seqs, self.p.Hq, self.p.D)
+        om, ol, oo = (x // 4 for x in self.pda.pda_state_offsets(self.dims()))
+        return s[om:om + r].reshape(self.max_seqs, self.p.Hq), s[ol:ol + r].reshape(self.max_seqs, self.p.Hq), \
+            s[oo:oo + r * self.p.D].reshape(self.max_seqs, self.p.Hq, self.p.D)
 
 
 def out_to_f64(out) -> np.ndarray:

@@ -223,10 +223,12 @@ def test_attn_paged_prefill_wrapper():
         assert case.k_base == 0 and case.v_base == npages
         q = torch.from_numpy(case.qc.view(np.int16)).to(dev.dev).view(torch.bfloat16)
         lens = torch.tensor(ctx, dtype=torch.int32)
-        for mask in (None, rng.random((S, 48)) >= 0.2, rng.random((S, Q, 48)) >= 0.2):
+        for k, mask in enumerate((None, rng.random((S, 48)) >= 0.2, rng.random((S, Q, 48)) >= 0.2)):
             tm = None if mask is None else torch.from_numpy(mask)
+            # the last call on a side stream (temporaries made on the current one)
+            side = torch.cuda.Stream() if k == 2 else None
             out = pda.attn_paged_prefill(q, kc.view(torch.bfloat16), vc.view(torch.bfloat16),
-                                         dev.blocks[0], lens, is_causal=True, mask=tm)
+                                         dev.blocks[0], lens, is_causal=True, mask=tm, stream=side)
             torch.cuda.synchronize()
             got = out_to_f64(out.view(torch.int16))
             ref = oracle_prefill(case, causal=True, mask=mask)["out"]

@@ -102,16 +102,36 @@ def test_state_and_workspace_sizes():
     for bps in (1, 3, 32, 100):
         eff = min(bps, 32)
         assert pda.pda_blocks_per_split(d, bps) == eff
-        # 64 control ints, then the partials: one slot per split of a
-        # sequence of up to ceil(32 / bps) splits
+        # 256 bytes of control words, the arrival counters, then the
+        # partials: one slot per split of a sequence of up to ceil(32 / bps)
+        # splits; (m, l) pairs padded to 16 bytes
         slots = -(-32 // eff)
-        assert pda.pda_workspace_bytes(d, bps) == 64 * 4 + rows * slots * (64 + 2) * 4
+        ml = -(-(rows * slots * 2 * 4) // 16) * 16
+        arrive = 4 * 2 * 8    # one 64-bit arrival counter per (sequence, kv head)
+        assert pda.pda_workspace_bytes(d, bps) == 256 + arrive + ml + rows * slots * 64 * 4
     auto = pda.pda_blocks_per_split(d, 0)
     assert 1 <= auto <= 32
     assert pda.pda_workspace_bytes(d, 0) >= pda.pda_workspace_bytes(d, auto)
     big = dims(tile_capacity=4096)
     assert pda.pda_blocks_per_split(big, 0) >= 4096 // 256
     assert pda.pda_state_bytes(dims(num_q_heads=6, num_kv_heads=4)) == 0
+
+
+@pytest.mark.parametrize("max_seqs,hq,hkv,bps", [(1, 9, 3, 1), (3, 5, 5, 3), (1, 1, 1, 7), (7, 3, 1, 2)])
+def test_regions_start_16_byte_aligned(max_seqs, hq, hkv, bps):
+    """The state's o rows and the workspace's o partials start on 16-byte
+    boundaries whatever the row counts (odd q-head counts included): the
+    kernels write them 16 bytes at a time."""
+    d = dims(max_seqs=max_seqs, num_q_heads=hq, num_kv_heads=hkv, tile_capacity=9)
+    rows = max_seqs * hq
+    offs = pda.pda_state_offsets(d)
+    assert all(o % 16 == 0 for o in offs)
+    assert offs[1] >= rows * 4 and offs[2] >= offs[1] + rows * 4
+    assert pda.pda_state_bytes(d) == offs[2] + rows * 64 * 4
+    slots = -(-9 // bps)
+    ml = rows * slots * 2 * 4
+    arrive = -(-(max_seqs * hkv * 8) // 16) * 16    # G <= 16: one head chunk per kv head
+    assert pda.pda_workspace_bytes(d, bps) == 256 + arrive + (-(-ml // 16) * 16) + rows * slots * 64 * 4
 
 
 FAKE = 1 << 20          # a 16-byte aligned host-side address that is never dereferenced
