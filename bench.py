@@ -1,7 +1,8 @@
 """Benchmark: paged GQA decode (and prefill) attention on one MI355X.
 
-One step is one pda_decode call (split-KV attention kernel + log-sum-exp merge
-kernel) over the ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
+One step is one pda_decode call (one launch of the split-KV attention kernel,
+whose last item per head group merges the splits by log-sum-exp) over the
+ragged batch-64 workload: 64 sequences, 32 q / 8 kv heads,
 head_dim 128, block_size 16, contexts log-uniform in [128, 32768], 1 % of keys
 scaled by 4, paged layout (workload "ragged-b64"; the other named workloads
 run the same way, tiled ones as begin_step + step_tile per tile + finalize).  Inputs
@@ -15,8 +16,11 @@ within 2 %: after an idle period the first tens of milliseconds run up to
 device synchronisations give `value` and `ms_per_step`; then 5 batches of
 >= --batch-ms each (event-timed on the launch stream) give the median and
 spread in `steady_state`.  `roofline.achieved` comes from the attention
-kernel's own average duration, taken with an event pair around each of its
-launches in a further pass over K steps; `roofline.traffic` from the
+kernel's own average duration: where the step launches that kernel alone
+(pda_decode), the event pair around the K timed steps; where it launches
+others too (begin_step, finalize), an event pair around each of its launches
+in a further pass over K steps (that figure is also reported for pda_decode,
+as `kernel_us_per_launch_event_bracketed`); `roofline.traffic` from the
 committed counter summary when the kernel sources still match it.  A
 workload whose K/V bytes would sit in the 256 MB last-level cache
 (llama3-8b-b16) rotates over enough copies of its pool (>= 7, >= 1 GiB) that
@@ -411,15 +415,24 @@ def main():
     nbytes = w.algorithmic_bytes()
     ms = m["wall_us"] / 1e3
     tbs = nbytes / (ms * 1e-3) / 1e12
-    kernel_us = None
+    kernel_us = bracketed_us = None
     if n_ev:
-        kernel_us = sum(b.elapsed_time(a) for b, a in zip(ev_b, ev_a)) * 1e3 / n_ev
+        bracketed_us = sum(b.elapsed_time(a) for b, a in zip(ev_b, ev_a)) * 1e3 / n_ev
+        kernel_us = bracketed_us
+    name = ("prefill_kernel at q_len 1" if args.decode_via_prefill else
+            "attend_kernel (paged split-KV attention)")
+    how = "average over the timed launches, each bracketed by its own event pair"
+    if n_ev and T == 1:
+        # the step launches this one kernel and nothing else, so the event
+        # pair around the timed region brackets its launches back to back
+        # (an event pair around each launch adds a few microseconds to it)
+        kernel_us = m["event_us"]
+        how = "average over the timed region's back-to-back launches (the step's only kernel)"
     # the step's algorithmic bytes, spread evenly over its attention launches
     bytes_per_launch = nbytes / launches
     if kernel_us:
         achieved_gbs = bytes_per_launch / (kernel_us * 1e-6) / 1e9
-        kernel_desc = ("prefill_kernel at q_len 1" if args.decode_via_prefill else
-                       "attend_kernel (paged split-KV attention)") + ", average over the timed launches"
+        kernel_desc = f"{name}, {how}"
     else:
         achieved_gbs = nbytes / (m["event_us"] * 1e-6) / 1e9
         kernel_desc = f"{api} step (all launches)"
@@ -453,6 +466,7 @@ def main():
                        "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                        "algorithmic_bytes_per_launch": int(bytes_per_launch),
                        "kernel_us_per_launch": round(kernel_us, 2) if kernel_us else None,
+                       "kernel_us_per_launch_event_bracketed": round(bracketed_us, 2) if bracketed_us else None,
                        "launches_per_step": launches}
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle)")
