@@ -239,8 +239,12 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             wsum_f[kMWaves + w] = nspl;
         }
         __syncthreads();
-        tot = wsum_f[0] + wsum_f[1] + wsum_f[2] + wsum_f[3];
-        nspl = wsum_f[4] + wsum_f[5] + wsum_f[6] + wsum_f[7];
+        tot = 0.f;
+        nspl = 0.f;
+        for (int ww = 0; ww < kMWaves; ++ww) {
+            tot += wsum_f[ww];
+            nspl += wsum_f[kMWaves + ww];
+        }
         const float waves = (float)((int)gridDim.x * kMWaves);
         if (tot * (float)units >= (float)kBigTokensLarge * waves) {
             big = max(1, kBigTokensLarge / span);

@@ -243,3 +243,23 @@ def dense_prefill_reference(case: Case, keep=None, sdpa_causal=False):
         o[~rows] = 0.0
         out[s] = o
     return out
+
+
+def workload_vmax(w):
+    """max |V| over each sequence's listed tokens, per (sequence, kv head,
+    element): float64 [S, Hkv, D], gathered from the workload's pool."""
+    blk, tok, kvh = w.strides
+    D, bs = w.head_dim, w.block_size
+    out = np.zeros((w.num_seqs, w.num_kv_heads, D))
+    for s in range(w.num_seqs):
+        n = int(w.contexts[s])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        pages = np.asarray(w.seq_blocks[s], dtype=np.int64)[t // bs]
+        base = w.v_base + pages * blk + (t % bs) * tok                       # [n]
+        idx = base[:, None, None] + np.arange(w.num_kv_heads)[None, :, None] * kvh \
+            + np.arange(D)[None, None, :]                                       # [n, Hkv, D]
+        v = bf16_bits_to_f32(w.pool[idx]).astype(np.float64)
+        out[s] = np.abs(v).max(axis=0)
+    return out

@@ -81,6 +81,29 @@ def test_small_shapes(shape, bps):
         assert_parity(got, ref_all["out"], label=f"decode {shape}")
 
 
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("bps", [128, "cap"])
+@pytest.mark.parametrize("T", [1, 2])
+def test_items_crossing_page_windows(bs, bps, T):
+    """Work items longer than 64 pages (blocks_per_split 128, and the whole
+    tile capacity), so that the 64-page window of page ids moves inside an
+    item on the block_size % 16 == 0 path: decode and tiled."""
+    S, Hq, Hkv, D = 3, 8, 2, 128
+    ctx = [2000, 5000, 3333]
+    announce("page windows", "bs", bs, "bps", bps, "tiles", T)
+    rng = np.random.Generator(np.random.PCG64(1000 + bs + T))
+    case = build_case(rng, S, Hq, Hkv, D, bs, ctx, layout="paged", n_tiles=T)
+    dev = Device(case)
+    b = dev.p.cap if bps == "cap" else bps
+    assert b * bs > 64 * bs and max(ctx) > 64 * bs   # items do cross windows
+    ref = oracle_of(dev)
+    state, out = dev.tiled(bps=b)
+    assert_parity(out_to_f64(out), ref["out"], label=f"tiled bs {bs} bps {b} tiles {T}")
+    if T == 1:
+        got = out_to_f64(dev.decode(bps=b))
+        assert_parity(got, ref["out"], label=f"decode bs {bs} bps {b}")
+
+
 def test_context_one_bit_exact():
     announce("context 1 bit-exact")
     rng = np.random.Generator(np.random.PCG64(31))

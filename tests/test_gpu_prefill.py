@@ -12,7 +12,7 @@ import pytest
 import oracle
 import workloads
 from gpu_harness import Device, assert_parity, out_to_f64
-from helpers import prefill_case
+from helpers import prefill_case, workload_vmax
 
 pytestmark = pytest.mark.gpu
 
@@ -55,14 +55,23 @@ def oracle_prefill(case, causal=True, mask=None, rows=None):
     return oracle.prefill(**case.prefill_args(), causal=causal, mask=mask, rows=rows)
 
 
+def assert_arith_bound(got, ref, vm, label):
+    """The per-element bound derived from the kernel's arithmetic: the softmax
+    weights enter the P.V product rounded to bf16 (relative error <= 2^-9
+    each; l sums the same rounded weights, so the result is an exact average
+    under slightly moved weights, off by at most 2^-9 max_t |v_t - out| <=
+    2^-9 (max_t |v_t| + |out|)), the result is rounded to bf16 once more
+    (2^-9 |out|, doubled for margin), and fp32 accumulation adds 1e-4.  `vm`
+    is max_t |v_t| per element over (at least) the keys the row attends to,
+    broadcastable to `ref`."""
+    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * (vm + np.abs(ref)) + 1e-4
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), (f"{label}: {bad.sum()} elements beyond the arithmetic bound; worst "
+                           f"{np.abs(got - ref)[bad].max():.3e} at {np.argwhere(bad)[0]}")
+
+
 def check(got, ref, case, label):
-    """The output gate (max 2e-2, mean 2e-3), then a per-element bound derived
-    from the kernel's arithmetic: the softmax weights enter the P.V product
-    rounded to bf16 (relative error <= 2^-9 each; l sums the same rounded
-    weights, so the result is an exact average under slightly moved weights,
-    off by at most 2^-9 max_t |v_t - out| <= 2^-9 (max_t |v_t| + |out|)), the
-    result is rounded to bf16 once more (2^-9 |out|, doubled for margin), and
-    fp32 accumulation adds 1e-4."""
+    """The output gate (max 2e-2, mean 2e-3), then the arithmetic bound."""
     assert_parity(got, ref, tight=False, label=label)
     S, Q, Hq, D = ref.shape
     G = case.Hq // case.Hkv
@@ -71,10 +80,9 @@ def check(got, ref, case, label):
         if case.V[s].shape[0]:
             vmax[s] = np.abs(case.V[s]).max(axis=0)
     vm = np.repeat(vmax, G, axis=1)[:, None, :, :]            # [S, 1, Hq, D]
-    bound = 2.0 ** -8 * np.abs(ref) + 2.0 ** -9 * (vm + np.abs(ref)) + 1e-4
-    bad = np.abs(got - ref) > bound
-    assert not bad.any(), (f"{label}: {bad.sum()} elements beyond the arithmetic bound; worst "
-                           f"{np.abs(got - ref)[bad].max():.3e} at {np.argwhere(bad)[0]}")
+    assert_arith_bound(got, ref, vm, label)
+
+
 
 
 SMALL = [
@@ -250,4 +258,11 @@ def test_prefill_full_size_sampled(name):
     rows = np.unique(np.concatenate([rng.integers(0, S * Q * Hq, size=1500),
                                      [0, S * Q * Hq - 1]]))
     ref = oracle.prefill_workload(w, rows=rows)["out"]
-    assert_parity(got.reshape(-1, D)[rows], ref, tight=False, label=name)
+    g = got.reshape(-1, D)[rows]
+    assert_parity(g, ref, tight=False, label=name)
+    # the arithmetic bound, with max |v| over all of the row's sequence's keys
+    # (at least the keys the row attends to)
+    vmax = workload_vmax(w)
+    seq = rows // (Q * Hq)
+    kvh = (rows % Hq) // (Hq // w.num_kv_heads)
+    assert_arith_bound(g, ref, vmax[seq, kvh], name)

@@ -114,3 +114,31 @@ def test_llama3_b16_sizes():
     w = workloads.named("llama3-8b-b16")
     assert w.num_seqs == 16 and 512 <= w.contexts.min() and w.contexts.max() <= 4096
     assert w.strides == (16384, 1024, 128)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill-2048"])
+def test_workload_vmax_matches_a_row_by_row_gather(name):
+    """The vectorised V gather behind the full-size prefill bound, against a
+    plain loop over (sequence, token, kv head) rows through row_start; a
+    wrong index would also pick up the poison (NaN) of unlisted pages."""
+    from helpers import workload_vmax
+    w = workloads.named(name)
+    got = workload_vmax(w)
+    assert np.all(np.isfinite(got))
+    S, Hkv, D, bs = w.num_seqs, w.num_kv_heads, w.head_dim, w.block_size
+    rng = np.random.default_rng(3)
+    for s in range(S):
+        n = int(w.contexts[s])
+        toks = range(n) if n <= 64 else sorted(rng.choice(n, 64, replace=False))
+        for g in range(Hkv):
+            for t in toks:
+                st = w.row_start(w.v_base, int(w.seq_blocks[s][t // bs]), t % bs, g)
+                v = np.abs(workloads.bf16_bits_to_f32(w.pool[st:st + D]).astype(np.float64))
+                assert np.all(v <= got[s, g]), (s, g, t)
+        if n <= 64:   # every row visited: the maximum is attained
+            for g in range(Hkv):
+                m = np.zeros(D)
+                for t in range(n):
+                    st = w.row_start(w.v_base, int(w.seq_blocks[s][t // bs]), t % bs, g)
+                    m = np.maximum(m, np.abs(workloads.bf16_bits_to_f32(w.pool[st:st + D])))
+                np.testing.assert_array_equal(m, got[s, g])
