@@ -40,7 +40,9 @@
  *    text with details is available from pda_last_error().
  *  - bf16 tensors hold raw bfloat16 bit patterns (uint16).  q, the pools, the
  *    output, the state and the workspace must be 16-byte aligned; strides must
- *    be multiples of 8 elements; page-id, count and last-valid arrays must be
+ *    be non-negative multiples of 8 elements (PDA_ERR_ALIGN) below 2^32
+ *    elements each, with a token row's offset inside a page below 2^31
+ *    (PDA_ERR_DIMS); page-id, count and last-valid arrays must be
  *    4-byte aligned.
  *  - Device-side data contract (not checkable on the host): counts are read
  *    clamped to [0, tile_capacity] and last-valid counts to [0, block_size];

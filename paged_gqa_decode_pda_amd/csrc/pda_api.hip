@@ -163,9 +163,13 @@ pda_status check_strides(const pda_dims *d, pda_strides st) {
     if (st.blk % 8 || st.tok % 8 || st.kvh % 8)
         return fail(PDA_ERR_ALIGN, "strides (%lld, %lld, %lld) must be multiples of 8 elements",
                     (long long)st.blk, (long long)st.tok, (long long)st.kvh);
-    const int64_t in_page = (int64_t)(d->block_size - 1) * st.tok +
-                            (int64_t)(d->num_kv_heads - 1) * st.kvh + d->head_dim;
-    if (in_page >= (int64_t(1) << 31))
+    // below 2^32 each, a 32-bit page id times the page stride fits 64 bits
+    if (st.blk >= (int64_t(1) << 32) || st.tok >= (int64_t(1) << 32) || st.kvh >= (int64_t(1) << 32))
+        return fail(PDA_ERR_DIMS, "strides (%lld, %lld, %lld) must be below 2^32 elements",
+                    (long long)st.blk, (long long)st.tok, (long long)st.kvh);
+    const __int128 in_page = (__int128)(d->block_size - 1) * st.tok +
+                             (__int128)(d->num_kv_heads - 1) * st.kvh + d->head_dim;
+    if (in_page >= (__int128(1) << 31))
         return fail(PDA_ERR_DIMS, "a token row offset inside a page exceeds 2^31 elements");
     return PDA_OK;
 }
@@ -723,7 +727,11 @@ pda_status pda_debug_time_attention(void *before, void *after) {
     return PDA_OK;
 }
 
-const char *pda_status_string(pda_status s) {
+const char *pda_status_string(pda_status status) {
+    // a C caller may pass any int: read it as one rather than as the enum
+    int s = 0;
+    static_assert(sizeof(status) == sizeof(s), "pda_status is int-sized");
+    memcpy(&s, &status, sizeof s);
     switch (s) {
         case PDA_OK: return "PDA_OK";
         case PDA_ERR_NULL: return "PDA_ERR_NULL";

@@ -913,7 +913,7 @@ hipError_t launch_d(const Plan &p, const AttendArgs &a, int cus, hipStream_t st,
 Plan choose_plan(int G, int D, int bs) {
     Plan p;
     p.dp = D <= 64 ? 64 : (D <= 128 ? 128 : 256);
-    p.nhc = (G + kHeadsPerItem - 1) / kHeadsPerItem;
+    p.nhc = G / kHeadsPerItem + (G % kHeadsPerItem != 0);   // ceil, without overflow for any G
     p.p16 = (bs % 16) == 0;
     return p;
 }

@@ -155,6 +155,9 @@ def test_decode_validation_before_enqueue():
         (dict(strides=(st[0], st[1] + 4, st[2])), pda.PDA_ERR_ALIGN),
         (dict(strides=(-st[0], st[1], st[2])), pda.PDA_ERR_ALIGN),
         (dict(strides=(st[0], 1 << 30, st[2])), pda.PDA_ERR_DIMS),
+        (dict(strides=(1 << 32, st[1], st[2])), pda.PDA_ERR_DIMS),
+        (dict(strides=((1 << 63) - 8, st[1], st[2])), pda.PDA_ERR_DIMS),
+        (dict(strides=(st[0], (1 << 63) - 8, st[2])), pda.PDA_ERR_DIMS),
         (dict(num_seqs=5), pda.PDA_ERR_MAX_SEQS),
         (dict(num_seqs=-1), pda.PDA_ERR_MAX_SEQS),
         (dict(workspace_bytes=16), pda.PDA_ERR_WORKSPACE),
