@@ -54,6 +54,13 @@ namespace {
 constexpr int kMWaves = 4;
 constexpr int kMThreads = 64 * kMWaves;
 
+// Scores on the VALU (v_dot2c_f32_bf16) instead of the matrix cores, for
+// items of up to kValuScoreHeads q heads: the measured alternative to the
+// MFMA score product, kept buildable for that comparison (off: the kernel
+// computes every score on the matrix cores).
+constexpr bool kValuScores = false;
+constexpr int kValuScoreHeads = 4;
+
 typedef __bf16 bf16x8_m __attribute__((ext_vector_type(8)));
 typedef float f32x4_m __attribute__((ext_vector_type(4)));
 typedef short i16x4_m __attribute__((ext_vector_type(4)));
@@ -93,6 +100,9 @@ struct MItem {
     int cb;          // first page (index into the sequence's list) of the page-id window
     int bidvec;      // the window: lane i holds the id of page cb + i
     u32x4 q[MShape<DP>::NCK];   // B operand: head lane%16, elements 32 c + 8 (lane/16) .. + 8
+    // VALU scores: q heads 0 .. kValuScoreHeads - 1 of the item, elements
+    // 32 c + 8 (lane/16) .. + 8 (the K elements the lane holds)
+    u32x4 qv[kValuScores ? kValuScoreHeads : 1][kValuScores ? MShape<DP>::NCK : 1];
 };
 
 // One claim on a launch-tagged counter (epoch << 32 | count), made by one
@@ -182,6 +192,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 
     __shared__ __attribute__((aligned(16))) unsigned char vt_all[kMWaves][SH::NTB][SH::TILE];
     __shared__ int scan[3 * kMWaves];
+    __shared__ float vsc_all[kValuScores ? kMWaves : 1][kValuScores ? 256 : 1];   // VALU scores: [token][head]
     __shared__ float wsum_f[2 * kMWaves];
     extern __shared__ int prefix[];   // 3 (S + 1) ints when a.prefix_mode
 
@@ -394,6 +405,14 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         const uint16_t *qp = a.q + ((int64_t)x.s * a.Hq + x.h0 + min(col, x.nh - 1)) * a.D;
 #pragma unroll
         for (int c = 0; c < NCK; ++c) x.q[c] = ld16(qp + kd[c]);
+        if constexpr (kValuScores) {
+#pragma unroll
+            for (int h = 0; h < kValuScoreHeads; ++h) {
+                const uint16_t *qh = a.q + ((int64_t)x.s * a.Hq + x.h0 + min(h, x.nh - 1)) * a.D;
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) x.qv[h][c] = ld16(qh + kd[c]);
+            }
+        }
         x.bidvec = a.blocks[(int64_t)x.s * a.cap + min(x.cb + lane, a.cap - 1)];
     };
 
@@ -406,6 +425,13 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 #pragma unroll
         for (int c = 0; c < NCK; ++c)
             x.q[c] = (col < x.nh && 32 * c + 8 * qd < a.D) ? x.q[c] : u32x4{0, 0, 0, 0};
+        if constexpr (kValuScores) {
+#pragma unroll
+            for (int h = 0; h < kValuScoreHeads; ++h)
+#pragma unroll
+                for (int c = 0; c < NCK; ++c)
+                    x.qv[h][c] = (32 * c + 8 * qd < a.D) ? x.qv[h][c] : u32x4{0, 0, 0, 0};
+        }
         if (x.kind != 0) return;
         if (ntok == 0) {
             x.kind = (!TILE && (a.prefix_mode || x.split == 0)) ? 1 : 2;
@@ -513,10 +539,46 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     auto scores = [&](const MItem<DP> &x, MGroup<DP> &r, int n) {
         const int gs = x.t0 + 16 * n;
         f32x4_m sacc = {0.f, 0.f, 0.f, 0.f};
+        bool valu = false;
+        if constexpr (kValuScores) valu = x.nh <= kValuScoreHeads;
+        if constexpr (kValuScores) if (valu) {
+            // lane (t, qd) = (lane % 16, lane / 16): the dot products of its
+            // quarter of K row t with the same quarter of each q head, summed
+            // over the four quarters' lanes, then transposed through LDS to
+            // the product's layout (lane: head lane % 16, tokens 4 qd + i)
+            float part[kValuScoreHeads];
 #pragma unroll
-        for (int c = 0; c < NCK; ++c)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_m, r.k[c]),
-                                                           __builtin_bit_cast(bf16x8_m, x.q[c]), sacc, 0, 0, 0);
+            for (int h = 0; h < kValuScoreHeads; ++h) {
+                part[h] = 0.f;
+#pragma unroll
+                for (int c = 0; c < NCK; ++c)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        // the elements go through scalars: a bit cast of a
+                        // vector element indexed in an unrolled loop compiles
+                        // to element 0 every time (seen with this hipcc)
+                        const uint32_t kk = r.k[c][j], qq = x.qv[h][c][j];
+                        part[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kk),
+                                                                 __builtin_bit_cast(bf16x2, qq), part[h], false);
+                    }
+                part[h] = sum4(part[h]);
+            }
+            float *vs = &vsc_all[kValuScores ? w : 0][0];
+            if (qd == 0) {
+#pragma unroll
+                for (int h = 0; h < kValuScoreHeads; ++h) vs[col * 16 + h] = part[h];
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[i] = col < kValuScoreHeads ? vs[(4 * qd + i) * 16 + col] : 0.f;
+            wave_lds_sync();
+        }
+        if (!valu) {
+#pragma unroll
+            for (int c = 0; c < NCK; ++c)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_m, r.k[c]),
+                                                               __builtin_bit_cast(bf16x8_m, x.q[c]), sacc, 0, 0, 0);
+        }
         // token validity: bit t of `ok` set when token gs + t takes part
         uint32_t okbits;
         if constexpr (MASK) {
