@@ -217,18 +217,19 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 
     // Work items.  With the prefix (up to kPrefixMaxSeqs sequences), each
     // sequence's splits are grouped: a share of them, `big` at a time, form
-    // "big" items queued first; the rest are single-split items queued after
-    // all big ones, so the queue ends with short work.  The single-split
-    // items of sequences that also have big items (long sequences, whose
-    // merges take many slots) come before those of the others, so that the
-    // launch ends with items whose merges are short.  Decode keeps one small
-    // item for an empty sequence so that its zero output row gets written.
+    // "big" items queued first; the rest, `sgl` at a time (the "single"
+    // items: one split, or two when the work is large), are queued after all
+    // big ones, so the queue ends with short work.  The single items of
+    // sequences that also have big items (long sequences, whose merges take
+    // many slots) come before those of the others, so that the launch ends
+    // with items whose merges are short.  Decode keeps one small item for an
+    // empty sequence so that its zero output row gets written.
     int nbig_pairs = 0, nlong_pairs = 0, npairs;
     int *pbig = prefix;                  // big items before sequence s
-    int *plong = prefix + a.S + 1;       // single-split items of sequences with big items, before s
-    int *pshort = prefix + 2 * (a.S + 1);   // single-split items of the others, before s
+    int *plong = prefix + a.S + 1;       // single items of sequences with big items, before s
+    int *pshort = prefix + 2 * (a.S + 1);   // single items of the others, before s
     const int nsp_max = (a.cap + a.bps - 1) / a.bps;
-    int big = 1, eighths = 0;
+    int big = 1, eighths = 0, sgl = 1;
     if (a.prefix_mode) {
         // Sizing (every workgroup takes the same decision from the same
         // totals): with at least kBigTokensLarge tokens of work per wave, big
@@ -260,6 +261,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         if (tot * (float)units >= (float)kBigTokensLarge * waves) {
             big = max(1, kBigTokensLarge / span);
             eighths = kEighthsLarge;
+            sgl = kSinglesLarge;
         } else if (nspl * (float)units > waves) {
             big = 2;
             eighths = kEighthsPaired;
@@ -274,7 +276,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             if (s < a.S) {
                 const int nsp = splits_of(pshort[s + 1], span);
                 nb = big_items_of(nsp, big, eighths);
-                ns = nsp - nb * big;
+                ns = (nsp - nb * big + sgl - 1) / sgl;
                 if (!TILE && nsp == 0) ns = 1;
                 if (nb > 0) {
                     nl = ns;
@@ -381,8 +383,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 x.slot = j;
             } else {
                 const int nb_s = __builtin_amdgcn_readfirstlane(pbig[x.s + 1] - pbig[x.s]);
-                x.split = nb_s * big + j;
-                x.nspl = 1;
+                x.split = nb_s * big + j * sgl;
+                x.nspl = sgl;
                 x.slot = nb_s + j;
             }
         } else {
@@ -670,9 +672,14 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     // acquire fence.  The wave's V-tile LDS (free between items) holds the
     // slot weights of 64 slots at a time.  Lanes take the (m, l) pairs LPH
     // lanes per head, and the o rows as flat 4-float chunks of the unit's
-    // [nh, D] block, U slots of loads in flight.
+    // [nh, D] block, two per lane per pass, U slots of loads in flight.
+    // The merge is a chain of dependent device-scope round trips at the end
+    // of the launch's last items, so when every lane's pairs fit R registers
+    // (the usual case) each pair is loaded once, together with the first U
+    // slots' o chunks.
     auto merge = [&](const MItem<DP> &x, int nslot) {
         constexpr int U = 8;
+        constexpr int R = 4;
         float *wl = reinterpret_cast<float *>(vt);   // [HPI][64] weights of one chunk of slots
         float *lsm = wl + HPI * 64;                  // [HPI] L per head
         float *fsm = lsm + HPI;                      // [HPI] tile: the state's weight per head
@@ -683,7 +690,130 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         const int hh = lane / lph, jl = lane - (lane / lph) * lph;
         const bool hok = hh < nh;
         const float *mlh = a.part_ml + (row0 + (hok ? hh : 0)) * a.nsplit * 2;
+        // 16-byte reads through a buffer resource over the unit's o rows
+        // (under 2 GiB: the host refuses larger ones)
+        const __amdgpu_buffer_rsrc_t urs =
+            unit_rsrc(a.part_o + row0 * a.nsplit * a.D, (uint32_t)((int64_t)nh * a.nsplit * a.D * 4));
+        const int D4 = a.D >> 2;
+        const int F4 = nh * D4;
+        // this lane's output chunk p0 + lane (+ 64 for the second): head,
+        // first element, byte offset of slot 0 (past F4: head 0, element 0,
+        // unused)
+        struct Chunk {
+            bool ok;
+            int h, d;
+            uint32_t obo;
+        };
+        auto chunk = [&](int c) {
+            Chunk k;
+            k.ok = c < F4;
+            k.h = k.ok ? c / D4 : 0;
+            k.d = k.ok ? 4 * (c - k.h * D4) : 0;
+            k.obo = (uint32_t)(((int64_t)k.h * a.nsplit * a.D + k.d) * 4);
+            return k;
+        };
+        auto store = [&](const Chunk &k, const f32x4_m &ov) {
+            if (!k.ok) return;
+            const int64_t r = row0 + k.h;
+            const float L = lsm[k.h];
+            if (TILE) {
+                const float fs = fsm[k.h];
+                float *po = a.o + r * a.D + k.d;
+                const f32x4_m st = *reinterpret_cast<const f32x4_m *>(po);
+                *reinterpret_cast<f32x4_m *>(po) = fs > 0.f ? st * fs + ov : ov;
+            } else {
+                u32x2 packed = {0u, 0u};
+                if (L > 0.f) {
+                    packed[0] = (uint32_t)f32_to_bf16(ov[0] / L) | ((uint32_t)f32_to_bf16(ov[1] / L) << 16);
+                    packed[1] = (uint32_t)f32_to_bf16(ov[2] / L) | ((uint32_t)f32_to_bf16(ov[3] / L) << 16);
+                }
+                *reinterpret_cast<u32x2 *>(a.out + r * a.D + k.d) = packed;
+            }
+        };
+        float ls_st = 0.f, ms_st = -INFINITY;
+        if (TILE && hok) {
+            ls_st = a.l[row0 + hh];
+            ms_st = a.m[row0 + hh] * kLog2e;
+        }
 
+        if (nslot <= 64 && nslot <= R * lph) {
+            // 1. the lane's pairs (slots jl + lph k) and the first U slots'
+            // o chunks of the first pass, in flight together
+            float mr[R], lr[R];
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int j = jl + lph * k;
+                mr[k] = -INFINITY;
+                lr[k] = 0.f;
+                if (j < nslot) ld_dev2(mlh + 2 * j, mr[k], lr[k]);
+            }
+            const Chunk k0 = chunk(lane), k1 = chunk(64 + lane);
+            f32x4_m x0[U], x1[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t jo = (uint32_t)min(u, nslot - 1) * (uint32_t)a.D * 4u;
+                x0[u] = ld_dev4b(urs, k0.obo + jo);
+                x1[u] = ld_dev4b(urs, k1.obo + jo);
+            }
+            // 2. each head's maximum over the slots holding tokens (and the
+            // state), the weights into LDS, L
+            float mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (lr[k] > 0.f) mx = fmaxf(mx, mr[k]);
+            if (TILE && hok && ls_st > 0.f) mx = fmaxf(mx, ms_st);
+            for (int off = 1; off < lph; off <<= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+            const float M = mx;
+            float lacc = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int j = jl + lph * k;
+                const float wgt = lr[k] > 0.f ? exp2_fast(mr[k] - M) : 0.f;
+                if (hok && j < nslot) wl[hh * 64 + j] = wgt;
+                lacc = fmaf(wgt, lr[k], lacc);
+            }
+            for (int off = 1; off < lph; off <<= 1) lacc += shfl_xor(lacc, off);
+            if (hok && jl == 0) {
+                const float fs = TILE && ls_st > 0.f ? exp2_fast(ms_st - M) : 0.f;
+                if (TILE) fsm[hh] = fs;
+                lsm[hh] = TILE ? fmaf(ls_st, fs, lacc) : lacc;
+            }
+            wave_lds_sync();
+            // 3. the weighted o rows, pass by pass (the weights stay in LDS)
+            for (int p0 = 0; p0 < F4; p0 += 128) {
+                const Chunk c0 = chunk(p0 + lane), c1 = chunk(p0 + 64 + lane);
+                f32x4_m o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+                for (int j0 = 0; j0 < nslot; j0 += U) {
+                    if (p0 != 0 || j0 != 0) {
+#pragma unroll
+                        for (int u = 0; u < U; ++u) {
+                            const uint32_t jo = (uint32_t)min(j0 + u, nslot - 1) * (uint32_t)a.D * 4u;
+                            x0[u] = ld_dev4b(urs, c0.obo + jo);
+                            x1[u] = ld_dev4b(urs, c1.obo + jo);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool in = j0 + u < nslot;
+                        const int jj = min(j0 + u, nslot - 1);
+                        o0 += (in ? wl[c0.h * 64 + jj] : 0.f) * x0[u];
+                        o1 += (in ? wl[c1.h * 64 + jj] : 0.f) * x1[u];
+                    }
+                }
+                store(c0, o0);
+                store(c1, o1);
+            }
+            if (TILE && hok && jl == 0) {
+                const float L = lsm[hh];
+                a.l[row0 + hh] = L;
+                a.m[row0 + hh] = L > 0.f ? M * kLn2 : -INFINITY;
+            }
+            wave_lds_sync();   // the tile LDS is the next groups' V tiles
+            return;
+        }
+
+        // More pairs than registers: the same, the pairs read again per chunk
+        // of 64 slots and per pass.
         // 1. each head's maximum over the slots holding tokens (and the state)
         float mx = -INFINITY;
 #pragma unroll 4
@@ -692,33 +822,15 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             ld_dev2(mlh + 2 * j, t[0], t[1]);
             if (t[1] > 0.f) mx = fmaxf(mx, t[0]);
         }
-        float ls_st = 0.f, ms_st = -INFINITY;
-        if (TILE && hok) {
-            ls_st = a.l[row0 + hh];
-            ms_st = a.m[row0 + hh] * kLog2e;
-            if (ls_st > 0.f) mx = fmaxf(mx, ms_st);
-        }
+        if (TILE && hok && ls_st > 0.f) mx = fmaxf(mx, ms_st);
         for (int off = 1; off < lph; off <<= 1) mx = fmaxf(mx, shfl_xor(mx, off));
         const float M = mx;   // the head's maximum, in its LPH lanes
         if (TILE && hok && jl == 0) fsm[hh] = ls_st > 0.f ? exp2_fast(ms_st - M) : 0.f;
 
-        // 2. passes of 64 chunks (two at a time): weights, L, weighted o rows,
-        // read 16 bytes at a time through a buffer resource over the unit's
-        // o rows (under 2 GiB: the host refuses larger ones).
-        const __amdgpu_buffer_rsrc_t urs =
-            unit_rsrc(a.part_o + row0 * a.nsplit * a.D, (uint32_t)((int64_t)nh * a.nsplit * a.D * 4));
-        const int D4 = a.D >> 2;
-        const int F4 = nh * D4;
+        // 2. passes of 128 chunks: weights, L, weighted o rows
         float lacc = 0.f;
         for (int p0 = 0; p0 < F4; p0 += 128) {
-            // this lane's two output chunks: (head, first element) of chunks
-            // p0 + lane and p0 + 64 + lane (past F4: head 0, element 0, unused)
-            const int c0 = p0 + lane, c1 = p0 + 64 + lane;
-            const bool ok0 = c0 < F4, ok1 = c1 < F4;
-            const int h0c = ok0 ? c0 / D4 : 0, h1c = ok1 ? c1 / D4 : 0;
-            const int d0c = ok0 ? 4 * (c0 - h0c * D4) : 0, d1c = ok1 ? 4 * (c1 - h1c * D4) : 0;
-            const uint32_t obo0 = (uint32_t)(((int64_t)h0c * a.nsplit * a.D + d0c) * 4);
-            const uint32_t obo1 = (uint32_t)(((int64_t)h1c * a.nsplit * a.D + d1c) * 4);
+            const Chunk c0 = chunk(p0 + lane), c1 = chunk(p0 + 64 + lane);
             f32x4_m o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
             for (int cb = 0; cb < nslot; cb += 64) {
                 const int n = min(64, nslot - cb);
@@ -737,15 +849,15 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const uint32_t jo = (uint32_t)(cb + min(j0 + u, n - 1)) * (uint32_t)a.D * 4u;
-                        x0[u] = ld_dev4b(urs, obo0 + jo);
-                        x1[u] = ld_dev4b(urs, obo1 + jo);
+                        x0[u] = ld_dev4b(urs, c0.obo + jo);
+                        x1[u] = ld_dev4b(urs, c1.obo + jo);
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const bool in = j0 + u < n;
                         const int jj = min(j0 + u, n - 1);
-                        o0 += (in ? wl[h0c * 64 + jj] : 0.f) * x0[u];
-                        o1 += (in ? wl[h1c * 64 + jj] : 0.f) * x1[u];
+                        o0 += (in ? wl[c0.h * 64 + jj] : 0.f) * x0[u];
+                        o1 += (in ? wl[c1.h * 64 + jj] : 0.f) * x1[u];
                     }
                 }
                 wave_lds_sync();   // the next chunk's weights overwrite these
@@ -755,26 +867,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 if (hok && jl == 0) lsm[hh] = TILE ? fmaf(ls_st, ls_st > 0.f ? fsm[hh] : 0.f, lacc) : lacc;
                 wave_lds_sync();
             }
-            auto store = [&](bool ok, int hcx, int dcx, const f32x4_m &ov) {
-                if (!ok) return;
-                const int64_t r = row0 + hcx;
-                const float L = lsm[hcx];
-                if (TILE) {
-                    const float fs = fsm[hcx];
-                    float *po = a.o + r * a.D + dcx;
-                    const f32x4_m st = *reinterpret_cast<const f32x4_m *>(po);
-                    *reinterpret_cast<f32x4_m *>(po) = fs > 0.f ? st * fs + ov : ov;
-                } else {
-                    u32x2 packed = {0u, 0u};
-                    if (L > 0.f) {
-                        packed[0] = (uint32_t)f32_to_bf16(ov[0] / L) | ((uint32_t)f32_to_bf16(ov[1] / L) << 16);
-                        packed[1] = (uint32_t)f32_to_bf16(ov[2] / L) | ((uint32_t)f32_to_bf16(ov[3] / L) << 16);
-                    }
-                    *reinterpret_cast<u32x2 *>(a.out + r * a.D + dcx) = packed;
-                }
-            };
-            store(ok0, h0c, d0c, o0);
-            store(ok1, h1c, d1c, o1);
+            store(c0, o0);
+            store(c1, o1);
         }
         if (TILE && hok && jl == 0) {
             const float L = lsm[hh];
@@ -853,7 +947,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const int before = lane == 0 ? (int)epoch_claim(a.arrive + (int64_t)x.s * units + x.unit, a.epoch) : 0;
-        const int nslot = slots_of(x.nsp, a.prefix_mode != 0, big, eighths);
+        const int nslot = slots_of(x.nsp, a.prefix_mode != 0, big, eighths, sgl);
         if (readlane(before, 0) == nslot - 1) {
             // this XCD's L2 may hold stale copies of the partials' lines
             // (from whatever last touched the workspace): invalidate it

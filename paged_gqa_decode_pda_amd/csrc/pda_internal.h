@@ -73,6 +73,11 @@ constexpr int kPrefixMaxSeqs = 10240;
 constexpr int kBigTokensLarge = 1024;
 constexpr int kEighthsLarge = 7;
 constexpr int kEighthsPaired = 6;
+// With at least kBigTokensLarge tokens of work per wave, the splits left
+// after the big items go kSinglesLarge at a time (the last item of a sequence
+// takes what remains): measured on MI355X, items of 512 tokens there beat 256
+// (fewer items and partial slots per sequence, so shorter merges).
+constexpr int kSinglesLarge = 2;
 
 // Optional events recorded on the launch stream right before and right after
 // the attention kernel (timing diagnostics); null members are skipped.
