@@ -217,9 +217,9 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 
     // Work items.  With the prefix (up to kPrefixMaxSeqs sequences), each
     // sequence's splits are grouped: a share of them, `big` at a time, form
-    // "big" items queued first; the rest, `sgl` at a time (the "single"
-    // items: one split, or two when the work is large), are queued after all
-    // big ones, so the queue ends with short work.  The single items of
+    // "big" items queued first; the rest (the "single" items: one split, or,
+    // for sequences with big items when the work is large, `sgl` splits) are
+    // queued after all big ones, so the queue ends with short work.  The single items of
     // sequences that also have big items (long sequences, whose merges take
     // many slots) come before those of the others, so that the launch ends
     // with items whose merges are short.  Decode keeps one small item for an
@@ -276,7 +276,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             if (s < a.S) {
                 const int nsp = splits_of(pshort[s + 1], span);
                 nb = big_items_of(nsp, big, eighths);
-                ns = (nsp - nb * big + sgl - 1) / sgl;
+                const int sg = nb > 0 ? sgl : 1;   // only long sequences pair their singles
+                ns = (nsp - nb * big + sg - 1) / sg;
                 if (!TILE && nsp == 0) ns = 1;
                 if (nb > 0) {
                     nl = ns;
@@ -383,8 +384,9 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 x.slot = j;
             } else {
                 const int nb_s = __builtin_amdgcn_readfirstlane(pbig[x.s + 1] - pbig[x.s]);
-                x.split = nb_s * big + j * sgl;
-                x.nspl = sgl;
+                const int sg = is_long ? sgl : 1;
+                x.split = nb_s * big + j * sg;
+                x.nspl = sg;
                 x.slot = nb_s + j;
             }
         } else {

@@ -139,14 +139,15 @@ __device__ __forceinline__ int splits_of(int ntok, int span) { return ntok > 0 ?
 
 // Work items of a sequence with nsp splits (prefix mode): nb "big" items of
 // `big` consecutive splits cover about eighths / 8 of the splits, then one
-// item per `sgl` remaining splits (the last takes what is left).  Items are
-// numbered in token order; item k of the sequence owns partial slot k, so a
-// sequence has nb + ceil((nsp - nb * big) / sgl) slots.
+// item per `sgl` remaining splits when nb > 0, else per split (the last item
+// takes what is left).  Items are numbered in token order; item k of the
+// sequence owns partial slot k.
 __device__ __forceinline__ int big_items_of(int nsp, int big, int eighths) { return (eighths * nsp) / (8 * big); }
 __device__ __forceinline__ int slots_of(int nsp, bool prefix_mode, int big, int eighths, int sgl) {
     if (!prefix_mode) return nsp;
     const int nb = big_items_of(nsp, big, eighths);
-    return nb + (nsp - nb * big + sgl - 1) / sgl;
+    const int sg = nb > 0 ? sgl : 1;
+    return nb + (nsp - nb * big + sg - 1) / sg;
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -73,10 +73,11 @@ constexpr int kPrefixMaxSeqs = 10240;
 constexpr int kBigTokensLarge = 1024;
 constexpr int kEighthsLarge = 7;
 constexpr int kEighthsPaired = 6;
-// With at least kBigTokensLarge tokens of work per wave, the splits left
-// after the big items go kSinglesLarge at a time (the last item of a sequence
+// With at least kBigTokensLarge tokens of work per wave, the splits that a
+// sequence with big items has left go kSinglesLarge at a time (the last item
 // takes what remains): measured on MI355X, items of 512 tokens there beat 256
-// (fewer items and partial slots per sequence, so shorter merges).
+// (fewer items and partial slots per sequence, so shorter merges), while the
+// short sequences that end the queue keep one split per item.
 constexpr int kSinglesLarge = 2;
 
 // Optional events recorded on the launch stream right before and right after
