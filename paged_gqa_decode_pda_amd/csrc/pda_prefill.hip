@@ -19,15 +19,21 @@
 //      operand) x P^T (B operand), 32 tokens deep, with the 32 tokens taken in
 //      the order (4(l/16) .. +3 of half 0, the same of half 1) that the
 //      scores left in the lanes.  V^T's lanes need 8 tokens of one column,
-//      so each 32-token V tile goes through LDS (row-major, 16-byte writes,
-//      2-byte transposed reads on a padded pitch that keeps the four lane
-//      groups on disjoint banks).  O^T's lanes hold row l%16, so the online
-//      softmax rescale of a row never leaves its lane.
+//      so V is read back from LDS with 2-byte transposed reads (the 16-byte
+//      chunks of a V row stored XOR-swizzled by the row, so the rows one
+//      read covers fall on disjoint banks).  O^T's lanes hold row l%16, so
+//      the online softmax rescale of a row never leaves its lane.
 //
-// Work items: (sequence, kv split, kv head, row tile) with the row tile
-// fastest; a wave takes one item (RB row blocks of 16 query rows, rows
-// r = i * G + (h - g G) of kv head g) and streams the split's tokens in steps
-// of 32, one step of loads ahead.  Units (sequence, kv split, kv head) are
+// Work items: (sequence, kv split, kv head, group of four row tiles); a
+// workgroup takes one, each of its four waves one row tile (RB row blocks of
+// 16 query rows, rows r = i * G + (h - g G) of kv head g), and they stream
+// the split's tokens in steps of 32 through a three-stage ring in LDS: K and
+// V of a step are loaded once for the four waves, straight from memory into
+// LDS (gfx950's global_load_lds_dwordx4, a quarter of the loads per wave),
+// two steps ahead, and every wave reads them from the ring (K in exactly the
+// product's operand layout).  One barrier per step: behind it every wave's
+// loads of the step have landed and every wave is done with the stage that
+// the next loads overwrite.  Units (sequence, kv split, kv head) are
 // dealt round-robin to the eight XCDs, longest first when there are few
 // enough (sequence, split) pairs to rank in each workgroup, and a unit's row
 // tiles, which read the same pages, run on consecutive waves of one XCD.
@@ -48,19 +54,93 @@ constexpr int kPfThreads = 64 * kPfWaves;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// LDS pitch (bytes) of one V row.  A transposing read covers 32 bytes of 16
-// consecutive rows; with 32 bytes of padding each row starts an odd multiple
-// of 8 banks after the previous one, so any 8 consecutive rows take 8
-// disjoint groups of 8 banks.
-template <int DP>
-struct PfTile {
-    static constexpr int kPitch = 2 * DP + 32;
-    static constexpr int kBytes = 32 * kPitch;
-};
-
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
+
+// One stage of the ring: a 32-token step's K, [half][chunk] blocks of 64
+// lanes x 16 bytes in the score product's A-operand layout (lane l: token
+// l % 16 of the half, elements 32 c + 8 (l / 16) .. + 7), then its V, 32
+// rows of 2 DP bytes whose 16-byte chunk c of row r sits at chunk position
+// c ^ 2 (r % 4): a transposing read takes 8 bytes of the same 32-byte piece
+// from each of 4 consecutive rows per 16 lanes, and the swizzle puts those
+// four pieces on disjoint groups of 8 banks whatever the pitch.
+template <int DP>
+struct PfStage {
+    static constexpr int NCK = DP / 32;          // 32-element chunks of the head dim
+    static constexpr int CPR = DP / 8;           // 16-byte chunks per V row
+    static constexpr int RPI = 64 / CPR;         // V rows per load instruction
+    static constexpr int NV = 32 / RPI;          // V load instructions per step
+    static constexpr int NJ = 2 * NCK + NV;      // load instructions per step (of 1 KB each)
+    static constexpr int KBYTES = 2 * NCK * 1024;
+    static constexpr int PITCH = 2 * DP;
+    static constexpr int BYTES = KBYTES + 32 * PITCH;
+};
+constexpr int kPfStages = 3;
+__device__ __forceinline__ int vswz(int row) { return 2 * (row & 3); }
+
+// s_waitcnt vmcnt(n) (expcnt, lgkmcnt left at their maxima), n < 64.
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 0xF) | ((n >> 4) << 14); }
+
+// A step's K from its ring stage: N reads of 16 bytes per lane at p + 1024 j
+// (p = the stage plus 16 * lane), waited for inside the block.  The ring's
+// data comes from DMA loads the caller has waited for (its own) and fenced
+// with a barrier (everyone's); written as asm because the compiler, which
+// cannot tell the stages apart, would otherwise wait for every load in
+// flight, the later steps' too, before the first read.  The outputs are
+// early-clobber: a read's result may land before a later read of the block
+// has taken its address, so no output may share the address register.
+#define PF_RD(j) "ds_read_b128 %" #j ", %[p] offset:" #j "*1024\n"
+__device__ __forceinline__ void lds_read_k(u32x4 (&k)[4], const lds_u8_t *p) {
+    asm volatile(PF_RD(0) PF_RD(1) PF_RD(2) PF_RD(3) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+                 : [p] "v"(p));
+}
+__device__ __forceinline__ void lds_read_k(u32x4 (&k)[8], const lds_u8_t *p) {
+    asm volatile(PF_RD(0) PF_RD(1) PF_RD(2) PF_RD(3) PF_RD(4) PF_RD(5) PF_RD(6) PF_RD(7)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+                   "=&v"(k[7])
+                 : [p] "v"(p));
+}
+__device__ __forceinline__ void lds_read_k(u32x4 (&k)[16], const lds_u8_t *p) {
+    asm volatile(PF_RD(0) PF_RD(1) PF_RD(2) PF_RD(3) PF_RD(4) PF_RD(5) PF_RD(6) PF_RD(7) PF_RD(8)
+                 PF_RD(9) PF_RD(10) PF_RD(11) PF_RD(12) PF_RD(13) PF_RD(14) PF_RD(15)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+                   "=&v"(k[7]), "=&v"(k[8]), "=&v"(k[9]), "=&v"(k[10]), "=&v"(k[11]), "=&v"(k[12]),
+                   "=&v"(k[13]), "=&v"(k[14]), "=&v"(k[15])
+                 : [p] "v"(p));
+}
+#undef PF_RD
+
+// Transposed V reads of head-dim blocks 4 m .. 4 m + 3 from a ring stage:
+// block 4 m + j at b[j] + OFF (rows 0 .. 15) and b[j] + OFF + HI (rows 16 ..
+// 31), waited for inside the block (for the reason given at lds_read_k).
+template <int OFF, int HI>
+__device__ __forceinline__ void lds_read_vt4(i16x4_t (&lo)[4], i16x4_t (&hi)[4], const lds_u8_t *b0,
+                                             const lds_u8_t *b1, const lds_u8_t *b2, const lds_u8_t *b3) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%c12\n"
+        "ds_read_b64_tr_b16 %1, %9 offset:%c12\n"
+        "ds_read_b64_tr_b16 %2, %10 offset:%c12\n"
+        "ds_read_b64_tr_b16 %3, %11 offset:%c12\n"
+        "ds_read_b64_tr_b16 %4, %8 offset:%c13\n"
+        "ds_read_b64_tr_b16 %5, %9 offset:%c13\n"
+        "ds_read_b64_tr_b16 %6, %10 offset:%c13\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:%c13\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+          "=&v"(hi[3])
+        : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "n"(OFF), "n"(OFF + HI));
+}
+
+// 16 bytes per lane from global memory into LDS at dst + 16 * lane (dst
+// wave-uniform; gfx950 global_load_lds_dwordx4, counted on vmcnt like a load).
+__device__ __forceinline__ void ld16_lds(const void *src, lds_u8_t *dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+}
 
 // The running max a row's weights are taken against moves only when the
 // row's true max exceeds it by more than this (log2 units): weights stay
@@ -109,20 +189,27 @@ __device__ __forceinline__ u32x4 ld16_at(const uint16_t *base, uint32_t byte_off
 // need the whole register file of one wave.
 template <int DP, int RB, bool MASK, bool P16, bool LAPS>
 __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) prefill_kernel(const PrefillArgs a) {
-    constexpr int NCK = DP / 32;          // 32-element chunks of the head dim
+    using SG = PfStage<DP>;
+    constexpr int NCK = SG::NCK, CPR = SG::CPR, RPI = SG::RPI, NV = SG::NV, NJ = SG::NJ;
     constexpr int NDB = DP / 16;          // 16-element blocks of the head dim (output)
-    constexpr int CPR = DP / 8;           // 16-byte chunks per V row
-    constexpr int RPI = 64 / CPR;         // V rows per load instruction
-    constexpr int NV = 32 / RPI;          // V load instructions per 32-token step
-    constexpr int PITCH = PfTile<DP>::kPitch;
-    __shared__ __attribute__((aligned(16))) unsigned char vt_all[kPfWaves][PfTile<DP>::kBytes];
+    constexpr int PITCH = SG::PITCH;
+    constexpr int SHARE = NJ / kPfWaves;  // load instructions per wave and step
+    static_assert(NJ % kPfWaves == 0, "every wave takes the same share of a step's loads");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[kPfStages * SG::BYTES];
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qd = lane >> 4, col = lane & 15;
-    unsigned char *vt = vt_all[w];
-    lds_u8_t *vt_lds = (lds_u8_t *)&vt_all[0][0] + w * PfTile<DP>::kBytes;   // the LDS address space
-    const uint32_t tr_off = (uint32_t)((4 * qd + (col >> 2)) * PITCH + 8 * (col & 3));
+    lds_u8_t *ring_lds = (lds_u8_t *)&ring[0];   // the LDS address space
+    // transposing reads of V: lane (qd, c) reads row 4 qd + c/4 (of each
+    // half), bytes 8 (c % 4) .. + 8 of the 32-byte piece of head-dim block n,
+    // which the swizzle stores at piece n ^ (c/4) of the row (row % 4 ==
+    // c/4); for n = 4 m + j that is 128 m + 32 (j ^ c/4): four lane offsets
+    // plus an immediate
+    uint32_t tr_b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        tr_b[j] = (uint32_t)(SG::KBYTES + (4 * qd + (col >> 2)) * PITCH + 8 * (col & 3) + 32 * (j ^ (col >> 2)));
 
     // Work assignment.  Hardware workgroup b runs on XCD b % 8 (the grid is
     // a multiple of 8).  Units (sequence, split, kv head), kv head fastest,
@@ -156,17 +243,21 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         }
         __syncthreads();
     }
-    // Each workgroup walks its XCD's list of four-item positions: position
-    // r, then 2R - 1 - r, then 2R + r, ... (R workgroups per XCD, at most
-    // as many as are resident), so no workgroup waits for dispatch and, with
-    // the list longest first, each pairs long work with short.  Without LAPS
-    // (the list fits the resident workgroups) there is one lap.
+    // Each workgroup walks its XCD's list of tile groups: position r, then
+    // 2R - 1 - r, then 2R + r, ... (R workgroups per XCD, at most as many as
+    // are resident), so no workgroup waits for dispatch and, with the list
+    // longest first, each pairs long work with short.  Without LAPS (the list
+    // fits the resident workgroups) there is one lap.  Every wave of the
+    // workgroup takes the same path through these loops (the barriers).
     const int R = (int)(gridDim.x >> 3);
+    const int ntg = (a.ntiles + kPfWaves - 1) / kPfWaves;   // tile groups per unit
     for (int64_t lap = 0; LAPS || lap == 0; ++lap) {
         const int64_t r = (lap & 1) ? (R - 1 - (b >> 3)) : (b >> 3);
-        const int64_t pos = (lap * R + r) * kPfWaves + w;   // position in XCD b % 8's item list
-        const int64_t k = pos / a.ntiles;
-        const int rt = (int)(pos - k * a.ntiles);
+        const int64_t pos = lap * R + r;   // position in XCD b % 8's list of tile groups
+        const int64_t k = pos / ntg;
+        const int tg = (int)(pos - k * ntg);
+        const int rt = tg * kPfWaves + w;   // this wave's row tile
+        const bool have = rt < a.ntiles;    // a wave past the unit's last tile only loads
         const int64_t u = (b & 7) + 8 * k;
         if (u >= (int64_t)npairs * a.Hkv) break;   // positions only grow with lap
         const int g = (int)(u % a.Hkv);
@@ -186,18 +277,17 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         int lim[RB];            // last key position the row keeps (-1: none)
         int64_t rowid[RB];      // (s Q + i) Hq + h, or -1 past the chunk
         const uint8_t *mrow[RB];  // the row's keep-mask bytes (with a mask)
-        int lim_max = -1, lim_min = 0x7fffffff;
+        int lim_min = 0x7fffffff;
         u32x4 qb[RB][NCK];
     #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             const int r = rt * 16 * RB + 16 * rb + col;
-            const bool ok = r < QG;
+            const bool ok = have && r < QG;
             const int i = ok ? r / a.G : 0;
             const int h = g * a.G + (ok ? r - i * a.G : 0);
             rowid[rb] = ok ? ((int64_t)s * a.Q + i) * a.Hq + h : -1;
             lim[rb] = ok ? (a.causal ? P - a.Q + i : P - 1) : -1;
             mrow[rb] = MASK ? a.mask + (int64_t)s * a.mask_ss + (int64_t)i * a.mask_qs : nullptr;
-            lim_max = max(lim_max, lim[rb]);
             if (ok) lim_min = min(lim_min, lim[rb]);
             const uint16_t *qp = a.q + (ok ? rowid[rb] : 0) * a.D;
     #pragma unroll
@@ -206,11 +296,13 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 qb[rb][c] = (ok && d0 < a.D) ? ld16(qp + d0) : u32x4{0, 0, 0, 0};
             }
         }
-        lim_max = __builtin_amdgcn_readfirstlane(wave_max_i(lim_max));
         lim_min = __builtin_amdgcn_readfirstlane(wave_min_i(lim_min));
-
+        // the workgroup's steps go as far as its last row keeps keys (the same
+        // in every wave); a wave's rows past their own limit mask the tokens
+        const int rlast = min((tg + 1) * kPfWaves * 16 * RB, QG) - 1;
+        const int lim_g = a.causal ? P - a.Q + rlast / a.G : P - 1;
         const int t0 = sp * span;
-        const int t1 = min(min(t0 + span, P), lim_max + 1);
+        const int t1 = min(min(t0 + span, P), lim_g + 1);
         const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
 
         float m2[RB], lsum[RB];
@@ -233,15 +325,25 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             const int d0 = 32 * c + 8 * qd;
             kd[c] = d0 < a.D ? d0 : 0;   // past head_dim: re-read chunk 0 (q is 0 there)
         }
-        const int vrow = lane / CPR;           // V row within a load instruction
-        const int vd = (lane % CPR) * 8;       // first V element of the lane
-        const int vdo = vd < a.D ? vd : 0;
+        // V load instruction v fills rows RPI v .. + RPI - 1 of the stage, lane
+        // l at chunk position l % CPR of row RPI v + l / CPR, so it loads the
+        // row's chunk (l % CPR) ^ 2 (row % 4): element offset vdo[v % 2] (row
+        // % 4 changes with v only when RPI == 2); past head_dim it re-reads
+        // chunk 0 (in bounds, never stored out)
+        const int vlr = lane / CPR;
+        int vdo[2];
+    #pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int vd = 8 * ((lane % CPR) ^ vswz(RPI * e + vlr));
+            vdo[e] = vd < a.D ? vd : 0;
+        }
         // lane byte offsets from a page row's start, for steps whose 16-token
         // halves each lie inside one page (block_size a multiple of 16)
         uint32_t kob[NCK];
     #pragma unroll
         for (int c = 0; c < NCK; ++c) kob[c] = 2u * (uint32_t)(col * (int)a.tok + kd[c]);
-        const uint32_t vob = 2u * (uint32_t)(vrow * (int)a.tok + vdo);
+        const uint32_t vob[2] = {2u * (uint32_t)(vlr * (int)a.tok + vdo[0]),
+                                 2u * (uint32_t)(vlr * (int)a.tok + vdo[1])};
         // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
         // 16-aligned and listed
         auto half_base = [&](int tb, int hf) -> int64_t {
@@ -258,13 +360,8 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
         };
 
-        // One register buffer each for K and V: the next step's V is requested
-        // as soon as the current one is in LDS, the next step's K as soon as the
-        // current step's score products have been issued.
-        u32x4 kr[2][NCK];   // [half][chunk]
-        u32x4 vr[NV];
         // The page-id window must cover step st's pages before the first load of
-        // that step is addressed (V of a step is requested before its K).
+        // that step is addressed.
         auto window_for = [&](int st) {
             const int tb = t0 + 32 * st;
             const int last = min(tb + 31, t1 - 1);
@@ -275,8 +372,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         };
-        // The two half bases of the step last addressed: K and V of a step read
-        // the same rows, so the (scalar) address arithmetic is done once per step.
+        // The two half bases of the step last addressed.
         int64_t hb[2] = {0, 0};
         int hb_step = -1;
         auto bases = [&](int st) {
@@ -287,55 +383,49 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 hb_step = st;
             }
         };
-        auto issue_k = [&](int st) {
+        // This wave's share of step st's loads (instructions j = w, w + 4,
+        // ...) into stage st % kPfStages: j < 2 NCK is K of half j / NCK,
+        // chunk j % NCK; the rest are V instructions.
+        auto issue = [&](int st) {
             const int tb = t0 + 32 * st;
+            lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
             window_for(st);
-            if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
-                bases(st);
+            const bool uni = P16 && tb + 32 <= t1;   // both halves whole pages' rows: uniform bases
+            if (uni) bases(st);
     #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const uint16_t *kb = a.k + hb[hf];
-    #pragma unroll
-                    for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16_at(kb, kob[c]);
-                }
-            } else {
-    #pragma unroll
-                for (int hf = 0; hf < 2; ++hf) {
-                    const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
-                    const uint16_t *kp = a.k + row_of(t);
-    #pragma unroll
-                    for (int c = 0; c < NCK; ++c) kr[hf][c] = ld16(kp + kd[c]);
-                }
-            }
-        };
-        auto issue_v = [&](int st) {
-            const int tb = t0 + 32 * st;
-            window_for(st);
-            if (P16 && tb + 32 <= t1) {
-                bases(st);
-                const uint16_t *vb[2] = {a.v + hb[0], a.v + hb[1]};
-    #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
-                    vr[v] = ld16_at(vb[hf] + (int64_t)r0 * a.tok, vob);
-                }
-            } else {
-    #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const int t = min(tb + RPI * v + vrow, t1 - 1);
-                    vr[v] = ld16(a.v + row_of(t) + vdo);
+            for (int j = 0; j < NJ; ++j) {
+                if (j % kPfWaves != w) continue;
+                if (j < 2 * NCK) {
+                    const int hf = j / NCK, c = j - hf * NCK;
+                    const void *src;
+                    if (uni) {
+                        src = reinterpret_cast<const char *>(a.k + hb[hf]) + kob[c];
+                    } else {
+                        const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
+                        src = a.k + row_of(t) + kd[c];
+                    }
+                    ld16_lds(src, stg + 1024 * j);
+                } else {
+                    const int v = j - 2 * NCK;
+                    const void *src;
+                    if (uni) {
+                        const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
+                        src = reinterpret_cast<const char *>(a.v + hb[hf] + (int64_t)r0 * a.tok) + vob[v & 1];
+                    } else {
+                        const int t = min(tb + RPI * v + vlr, t1 - 1);
+                        src = a.v + row_of(t) + vdo[v & 1];
+                    }
+                    ld16_lds(src, stg + SG::KBYTES + 1024 * v);
                 }
             }
         };
 
         auto compute = [&](int st) {
             const int tb = t0 + 32 * st;
-            // V tile into LDS, row-major (columns past head_dim are never stored
-            // out), then the next step's V requested into the same registers
-    #pragma unroll
-            for (int v = 0; v < NV; ++v)
-                *reinterpret_cast<u32x4 *>(vt + (RPI * v + vrow) * PITCH + 2 * vd) = vr[v];
-            if (st + 1 < nst) issue_v(st + 1);
+            const lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
+            // K of the step from the stage, in the product's operand layout
+            u32x4 kflat[2 * NCK];   // [half * NCK + chunk]
+            lds_read_k(kflat, stg + 16 * lane);
             // scores, transposed: lane -> row col, tokens 16 hf + 4 qd + i.  A
             // step inside every row's range (and the split's) keeps all tokens
             // and takes the path without per-token tests.
@@ -354,13 +444,12 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                     f32x4_t x = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
                     for (int c = 0; c < NCK; ++c)
-                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[hf][c]),
+                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kflat[hf * NCK + c]),
                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][c]), x,
                                                                     0, 0, 0);
                     sca[rb][hf] = x;
                 }
             }
-            if (st + 1 < nst) issue_k(st + 1);
             auto softmax = [&](auto full_c) {
                 constexpr bool FULL = decltype(full_c)::value;
     #pragma unroll
@@ -435,38 +524,68 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
             // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
             // 16 n + 4 (c % 4) .. + 3.
+            // head-dim blocks four at a time: their transposed reads, then
+            // their products
+            auto pv4 = [&](auto mc) {
+                constexpr int M = decltype(mc)::value;
+                i16x4_t lo4[4], hi4[4];
+                lds_read_vt4<128 * M, 16 * PITCH>(lo4, hi4, stg + tr_b[0], stg + tr_b[1], stg + tr_b[2],
+                                                  stg + tr_b[3]);
     #pragma unroll
-            for (int n = 0; n < NDB; ++n) {
-                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vt_lds + tr_off + 32 * n));
-                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4_t *)(vt_lds + tr_off + 16 * PITCH + 32 * n));
-                u32x4 A = {__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                           __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]};
-                if constexpr (MASK) {
-                    if (vkeep == 0) {
+                for (int j = 0; j < 4; ++j) {
+                    const int n = 4 * M + j;
+                    u32x4 A = {__builtin_bit_cast(u32x2, lo4[j])[0], __builtin_bit_cast(u32x2, lo4[j])[1],
+                               __builtin_bit_cast(u32x2, hi4[j])[0], __builtin_bit_cast(u32x2, hi4[j])[1]};
+                    if constexpr (MASK) {
+                        if (vkeep == 0) {
     #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t m = ((keep_any >> (2 * e)) & 1 ? 0xffffu : 0u) |
-                                               ((keep_any >> (2 * e + 1)) & 1 ? 0xffff0000u : 0u);
-                            A[e] &= m;
+                            for (int e = 0; e < 4; ++e) {
+                                const uint32_t m = ((keep_any >> (2 * e)) & 1 ? 0xffffu : 0u) |
+                                                   ((keep_any >> (2 * e + 1)) & 1 ? 0xffff0000u : 0u);
+                                A[e] &= m;
+                            }
                         }
                     }
-                }
     #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
-                                                                         __builtin_bit_cast(bf16x8_t, pb[rb]),
-                                                                         acc[rb][n], 0, 0, 0);
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[rb][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A),
+                                                                             __builtin_bit_cast(bf16x8_t, pb[rb]),
+                                                                             acc[rb][n], 0, 0, 0);
+                }
+            };
+            static_assert(NDB % 4 == 0 && NDB <= 16, "head-dim blocks in groups of four");
+            pv4(std::integral_constant<int, 0>{});
+            if constexpr (NDB > 4) pv4(std::integral_constant<int, 1>{});
+            if constexpr (NDB > 8) {
+                pv4(std::integral_constant<int, 2>{});
+                pv4(std::integral_constant<int, 3>{});
             }
             wave_lds_sync();
         };
 
-        if (nst > 0) {
-            issue_k(0);
-            issue_v(0);
+        // the item's q rows and page ids in registers before the ring's loads
+        // start (the compiler would otherwise wait for all loads in flight at
+        // every use of them)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        // the ring: steps st + 1 and st + 2 in flight while st is computed
+        if (nst > 0) issue(0);
+        if (nst > 1) issue(1);
+        for (int st = 0; st < nst; ++st) {
+            // this wave's loads of step st have landed (the next step's may
+            // still be in flight; loads complete in order), then everyone's
+            if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_wait(SHARE));
+            else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            // every wave is past step st - 1: its stage takes step st + 2
+            if (st + 2 < nst) issue(st + 2);
+            if (have) compute(st);
         }
-        for (int st = 0; st < nst; ++st) compute(st);
+        // every wave done with the ring before the next item's loads
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
         // totals: lane l holds O[row col][16 n + 4 qd + i]
     #pragma unroll
@@ -548,11 +667,11 @@ __global__ void __launch_bounds__(kPfThreads) prefill_merge_kernel(const Prefill
 template <int DP, int RB, bool MASK, bool P16>
 hipError_t launch_prefill_t(const PrefillArgs &args, hipStream_t st, const AttendEvents &ev) {
     PrefillArgs a = args;
-    // every XCD holds at most ceil(units / 8) units of ntiles items each; at
-    // most as many workgroups as are resident, each looping over positions
+    // every XCD holds at most ceil(units / 8) units of ceil(ntiles / 4)
+    // tile groups each; at most as many workgroups as are resident, each
+    // looping over positions
     const int64_t units = (int64_t)a.S * a.nsplit * a.Hkv;
-    const int64_t per_xcd = (units + 7) / 8 * a.ntiles;
-    const int64_t need = (per_xcd + kPfWaves - 1) / kPfWaves;   // positions per XCD
+    const int64_t need = (units + 7) / 8 * ((a.ntiles + kPfWaves - 1) / kPfWaves);   // positions per XCD
     const int64_t per_cu = (DP <= 128 && RB <= 2) ? 2 : 1;      // as the launch bounds allow
     const int64_t resident = (a.cus >= 8 ? a.cus / 8 : 1) * per_cu;   // per XCD
     const int64_t nwg = 8 * (need < resident ? need : resident);
