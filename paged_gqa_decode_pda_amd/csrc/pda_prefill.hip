@@ -200,6 +200,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qd = lane >> 4, col = lane & 15;
+    const u32x4 kOnes = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bf16 1.0 pairs
     lds_u8_t *ring_lds = (lds_u8_t *)&ring[0];   // the LDS address space
     // transposing reads of V: lane (qd, c) reads row 4 qd + c/4 (of each
     // half), bytes 8 (c % 4) .. + 8 of the 32-byte piece of head-dim block n,
@@ -305,12 +306,13 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         const int t1 = min(min(t0 + span, P), lim_g + 1);
         const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
 
-        float m2[RB], lsum[RB];
+        float m2[RB];
+        f32x4_t lacc[RB];   // the row's weight sum (all four elements)
         f32x4_t acc[RB][NDB];
     #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             m2[rb] = -INFINITY;
-            lsum[rb] = 0.f;
+            lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
             for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -319,31 +321,37 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         const int64_t gk = (int64_t)g * a.kvh;
         int cb = t0 / a.bs;   // first page of the page-id window
         int bidvec = brow[min(cb + lane, a.cap - 1)];
-        int kd[NCK];
+        // This wave's share of a step's loads: instructions j = w + 4 i.  The
+        // first NKI are K instructions (j < 2 NCK): half j / NCK, chunk j %
+        // NCK, lane l loading token l % 16 of the half, elements kdc[i] (32
+        // chunk + 8 (l / 16); past head_dim it re-reads chunk 0, where q is
+        // 0).  The other NVI are V instructions v = w + 4 (i - NKI): rows RPI
+        // v .. + RPI - 1 of the step, lane l at chunk position l % CPR of row
+        // RPI v + l / CPR, so it loads that row's chunk (l % CPR) ^ 2 (row %
+        // 4) (past head_dim chunk 0, never stored out).  Offsets in bytes
+        // from the first row of the instruction's half, for steps whose two
+        // 16-token halves each lie inside one page.
+        constexpr int NKI = NCK / 2, NVI = NV / 4;
+        static_assert(NKI + NVI == SHARE && NKI >= 1 && NVI >= 1, "load shares");
+        int khf[NKI], kdc[NKI], vhf[NVI], vtok[NVI], vdc[NVI];
+        uint32_t kob[NKI], vob[NVI];
     #pragma unroll
-        for (int c = 0; c < NCK; ++c) {
-            const int d0 = 32 * c + 8 * qd;
-            kd[c] = d0 < a.D ? d0 : 0;   // past head_dim: re-read chunk 0 (q is 0 there)
+        for (int i = 0; i < NKI; ++i) {
+            const int j = w + kPfWaves * i;
+            khf[i] = j / NCK;
+            const int d0 = 32 * (j - khf[i] * NCK) + 8 * qd;
+            kdc[i] = d0 < a.D ? d0 : 0;
+            kob[i] = 2u * (uint32_t)(col * (int)a.tok + kdc[i]);
         }
-        // V load instruction v fills rows RPI v .. + RPI - 1 of the stage, lane
-        // l at chunk position l % CPR of row RPI v + l / CPR, so it loads the
-        // row's chunk (l % CPR) ^ 2 (row % 4): element offset vdo[v % 2] (row
-        // % 4 changes with v only when RPI == 2); past head_dim it re-reads
-        // chunk 0 (in bounds, never stored out)
-        const int vlr = lane / CPR;
-        int vdo[2];
     #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int vd = 8 * ((lane % CPR) ^ vswz(RPI * e + vlr));
-            vdo[e] = vd < a.D ? vd : 0;
+        for (int i = 0; i < NVI; ++i) {
+            const int row = RPI * (w + kPfWaves * i) + lane / CPR;   // row of the step
+            vhf[i] = (RPI * (w + kPfWaves * i)) / 16;
+            vtok[i] = row;
+            const int vd = 8 * ((lane % CPR) ^ vswz(row));
+            vdc[i] = vd < a.D ? vd : 0;
+            vob[i] = 2u * (uint32_t)((row - 16 * vhf[i]) * (int)a.tok + vdc[i]);
         }
-        // lane byte offsets from a page row's start, for steps whose 16-token
-        // halves each lie inside one page (block_size a multiple of 16)
-        uint32_t kob[NCK];
-    #pragma unroll
-        for (int c = 0; c < NCK; ++c) kob[c] = 2u * (uint32_t)(col * (int)a.tok + kd[c]);
-        const uint32_t vob[2] = {2u * (uint32_t)(vlr * (int)a.tok + vdo[0]),
-                                 2u * (uint32_t)(vlr * (int)a.tok + vdo[1])};
         // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
         // 16-aligned and listed
         auto half_base = [&](int tb, int hf) -> int64_t {
@@ -383,39 +391,31 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 hb_step = st;
             }
         };
-        // This wave's share of step st's loads (instructions j = w, w + 4,
-        // ...) into stage st % kPfStages: j < 2 NCK is K of half j / NCK,
-        // chunk j % NCK; the rest are V instructions.
+        // This wave's share of step st's loads into stage st % kPfStages.
         auto issue = [&](int st) {
             const int tb = t0 + 32 * st;
             lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
             window_for(st);
-            const bool uni = P16 && tb + 32 <= t1;   // both halves whole pages' rows: uniform bases
-            if (uni) bases(st);
+            if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
+                bases(st);
     #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                if (j % kPfWaves != w) continue;
-                if (j < 2 * NCK) {
-                    const int hf = j / NCK, c = j - hf * NCK;
-                    const void *src;
-                    if (uni) {
-                        src = reinterpret_cast<const char *>(a.k + hb[hf]) + kob[c];
-                    } else {
-                        const int t = min(tb + 16 * hf + col, t1 - 1);   // past t1: a listed row, weight 0
-                        src = a.k + row_of(t) + kd[c];
-                    }
-                    ld16_lds(src, stg + 1024 * j);
-                } else {
-                    const int v = j - 2 * NCK;
-                    const void *src;
-                    if (uni) {
-                        const int hf = (RPI * v) / 16, r0 = RPI * v - 16 * hf;
-                        src = reinterpret_cast<const char *>(a.v + hb[hf] + (int64_t)r0 * a.tok) + vob[v & 1];
-                    } else {
-                        const int t = min(tb + RPI * v + vlr, t1 - 1);
-                        src = a.v + row_of(t) + vdo[v & 1];
-                    }
-                    ld16_lds(src, stg + SG::KBYTES + 1024 * v);
+                for (int i = 0; i < NKI; ++i)
+                    ld16_lds(reinterpret_cast<const char *>(a.k + (khf[i] ? hb[1] : hb[0])) + kob[i],
+                             stg + 1024 * (w + kPfWaves * i));
+    #pragma unroll
+                for (int i = 0; i < NVI; ++i)
+                    ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hb[1] : hb[0])) + vob[i],
+                             stg + SG::KBYTES + 1024 * (w + kPfWaves * i));
+            } else {   // rows past t1 read a listed row (weight 0)
+    #pragma unroll
+                for (int i = 0; i < NKI; ++i) {
+                    const int t = min(tb + 16 * khf[i] + col, t1 - 1);
+                    ld16_lds(a.k + row_of(t) + kdc[i], stg + 1024 * (w + kPfWaves * i));
+                }
+    #pragma unroll
+                for (int i = 0; i < NVI; ++i) {
+                    const int t = min(tb + vtok[i], t1 - 1);
+                    ld16_lds(a.v + row_of(t) + vdc[i], stg + SG::KBYTES + 1024 * (w + kPfWaves * i));
                 }
             }
         };
@@ -472,9 +472,9 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                         }
                         keep_any |= keep;
                     }
-                    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-                    mx = max4(mx) * a.scale_log2;
+                    float mx = fmax3_raw(fmax3_raw(sc[0][0], sc[0][1], sc[0][2]),
+                                         fmax3_raw(sc[0][3], sc[1][0], sc[1][1]), fmax_raw(sc[1][2], sc[1][3]));
+                    mx = max4_raw(mx) * a.scale_log2;
                     // move the reference max only when the row's max passes it by
                     // more than the slack (a row with nothing kept so far keeps
                     // (m, l, o) = (-inf, 0, 0))
@@ -494,11 +494,6 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                     }
                     pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                                    pack_bf16(p[6], p[7])};
-                    // l sums the weights as rounded for the product
-                    float ps = 0.f;
-    #pragma unroll
-                    for (int e = 0; e < 4; ++e) ps += bf_lo(pb[rb][e]) + bf_hi(pb[rb][e]);
-                    lsum[rb] = fmaf(lsum[rb], alpha[rb], ps);
                 }
             };
             if (full) softmax(std::true_type{});
@@ -508,6 +503,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 for (int rb = 0; rb < RB; ++rb) {
     #pragma unroll
                     for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
+                    lacc[rb] *= alpha[rb];
                 }
             }
             // tokens no row keeps get V = 0 (with a mask they may hold anything)
@@ -524,6 +520,14 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
             // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
             // 16 n + 4 (c % 4) .. + 3.
+            // l: the same product with a block of ones for V^T sums each
+            // row's weights exactly as rounded for P.V (every element of
+            // lacc holds the row's sum)
+    #pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kOnes),
+                                                                   __builtin_bit_cast(bf16x8_t, pb[rb]), lacc[rb],
+                                                                   0, 0, 0);
             // head-dim blocks four at a time: their transposed reads, then
             // their products
             auto pv4 = [&](auto mc) {
@@ -590,7 +594,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // totals: lane l holds O[row col][16 n + 4 qd + i]
     #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const float L = sum4(lsum[rb]);
+            const float L = lacc[rb][0];
             if (rowid[rb] < 0) continue;
             if (direct) {
                 uint16_t *op = a.out + rowid[rb] * a.D;
