@@ -26,11 +26,14 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
-# Per-source extra flags (none at present).  Forcing the prefill kernel's
-# MFMA results into VGPRs (-amdgpu-mfma-vgpr-form=1) removes the
-# accumulator copies between AGPRs and VGPRs but measured slower at 64 rows
-# per wave, the default shape.
-EXTRA_FLAGS = {}
+# Per-source extra flags.  The prefill kernel's scores never hold a NaN
+# (finite bf16 inputs; masked scores are -inf), so its translation unit is
+# built without NaN semantics: fmaxf on matrix-core results is then one
+# v_max_f32 instead of two quieting maxima and the maximum (infinities are
+# still honoured).  Forcing that kernel's MFMA results into VGPRs
+# (-amdgpu-mfma-vgpr-form=1) removes the accumulator copies between AGPRs
+# and VGPRs but measured slower at 64 rows per wave.
+EXTRA_FLAGS = {"pda_prefill.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

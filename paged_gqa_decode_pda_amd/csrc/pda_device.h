@@ -181,26 +181,6 @@ __device__ __forceinline__ float max4(float x) {
     pair32(fmaxf(a, b), a, b);
     return fmaxf(a, b);
 }
-// Maxima as single v_max_f32 / v_max3_f32 instructions.  fmaxf gets a
-// quieting v_max_f32 x, x on each operand that may hold a signalling NaN
-// (matrix-core results, for instance); the score paths never produce one,
-// so these skip it.
-__device__ __forceinline__ float fmax_raw(float a, float b) {
-    float r;
-    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-__device__ __forceinline__ float fmax3_raw(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-__device__ __forceinline__ float max4_raw(float x) {
-    float a, b;
-    pair16(x, a, b);
-    pair32(fmax_raw(a, b), a, b);
-    return fmax_raw(a, b);
-}
 // Sum over the same four lanes, in an order that is the same in every lane
 // (lanes with bit 4 clear first, then bit 5 clear first).
 __device__ __forceinline__ float sum4(float x) {

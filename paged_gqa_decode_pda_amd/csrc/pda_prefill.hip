@@ -306,12 +306,13 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         const int t1 = min(min(t0 + span, P), lim_g + 1);
         const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
 
-        float m2[RB];
-        f32x4_t lacc[RB];   // the row's weight sum (all four elements)
+        float m2[RB], thr[RB];   // the row's reference max (log2 units) and m2 + slack
+        f32x4_t lacc[RB];        // the row's weight sum (all four elements)
         f32x4_t acc[RB][NDB];
     #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             m2[rb] = -INFINITY;
+            thr[rb] = -INFINITY;
             lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
             for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -352,15 +353,6 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             vdc[i] = vd < a.D ? vd : 0;
             vob[i] = 2u * (uint32_t)((row - 16 * vhf[i]) * (int)a.tok + vdc[i]);
         }
-        // first element of the row of token tb + 16 hf (kv head g); tb + 16 hf is
-        // 16-aligned and listed
-        auto half_base = [&](int tb, int hf) -> int64_t {
-            const int th = tb + 16 * hf;
-            const int pg = page_of((uint32_t)th, a.bs_magic);
-            const int bid = __builtin_amdgcn_readlane(bidvec, pg - cb);
-            return (int64_t)bid * a.blk + gk + (int64_t)(th - pg * a.bs) * a.tok;
-        };
-
         // Element offset of token t's row (kv head g); t must be listed.
         auto row_of = [&](int t) -> int64_t {
             const int pg = page_of((uint32_t)t, a.bs_magic);
@@ -380,22 +372,42 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
         };
-        // The two half bases of the step last addressed.
-        int64_t hb[2] = {0, 0};
-        int hb_step = -1;
-        auto bases = [&](int st) {
-            if (hb_step != st) {
-                const int tb = t0 + 32 * st;
-                hb[0] = half_base(tb, 0);
-                hb[1] = half_base(tb, 1);
-                hb_step = st;
+        // Steps whose halves each lie inside one page address their loads
+        // from the halves' first rows.  Their page ids come through the
+        // scalar cache (the block table is read-only here, so the constant
+        // address space may serve it), fetched at the end of the step before
+        // the one that issues them: the fetch is in flight through the
+        // barrier wait, not in front of the LDS reads, which wait for every
+        // scalar load too.  No vector-to-scalar move or page-id window is on
+        // this path.
+        const __attribute__((address_space(4))) int32_t *brow_c =
+            (const __attribute__((address_space(4))) int32_t *)brow;
+        int pf_st = -1, pf_b[2] = {0, 0}, pf_r[2] = {0, 0};   // prefetched: step, page ids, rows in page
+        auto prefetch = [&](int st) {
+            const int tb = t0 + 32 * st;
+    #pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int pg = page_of((uint32_t)(tb + 16 * hf), a.bs_magic);
+                pf_b[hf] = brow_c[pg];
+                pf_r[hf] = tb + 16 * hf - pg * a.bs;
             }
+            pf_st = st;
+        };
+        // first element of each half's first row (kv head g); the strides are
+        // below 2^32 and in-page offsets below 2^31 (checked by the host), so
+        // 32-bit factors suffice
+        int64_t hb[2] = {0, 0};
+        const uint32_t blk32 = (uint32_t)a.blk, tok32 = (uint32_t)a.tok;
+        auto bases = [&](int st) {
+            if (pf_st != st) prefetch(st);
+    #pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+                hb[hf] = (int64_t)((uint64_t)(uint32_t)pf_b[hf] * blk32 + (uint32_t)pf_r[hf] * tok32) + gk;
         };
         // This wave's share of step st's loads into stage st % kPfStages.
         auto issue = [&](int st) {
             const int tb = t0 + 32 * st;
             lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
-            window_for(st);
             if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
                 bases(st);
     #pragma unroll
@@ -407,6 +419,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                     ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hb[1] : hb[0])) + vob[i],
                              stg + SG::KBYTES + 1024 * (w + kPfWaves * i));
             } else {   // rows past t1 read a listed row (weight 0)
+                window_for(st);
     #pragma unroll
                 for (int i = 0; i < NKI; ++i) {
                     const int t = min(tb + 16 * khf[i] + col, t1 - 1);
@@ -432,8 +445,8 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
             u32x4 pb[RB];
             int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
-            bool grow = false;
-            float alpha[RB];
+            int keep_rb[RB];    // the same for each row block's row
+            float lmx[RB];   // this lane's maximum scaled score per row block
             // every row block's score products, then the next step's K into the
             // same registers
             f32x4_t sca[RB][2];
@@ -450,15 +463,19 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                     sca[rb][hf] = x;
                 }
             }
-            auto softmax = [&](auto full_c) {
+            // Scores to weights.  The reference max of a row moves only when
+            // the row's max passes it by more than the slack (a row with
+            // nothing kept so far keeps (m, l, o) = (-inf, 0, 0)); while no
+            // lane of the wave passes its rows' threshold, no row moves and
+            // the cross-lane maxima are skipped.
+            auto scan = [&](auto full_c) -> bool {
                 constexpr bool FULL = decltype(full_c)::value;
+                bool pass = false;
     #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    f32x4_t sc[2] = {sca[rb][0], sca[rb][1]};
                     // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
-                    int keep = 0xff;
                     if constexpr (!FULL) {
-                        keep = 0;
+                        int keep = 0;
     #pragma unroll
                         for (int hf = 0; hf < 2; ++hf) {
     #pragma unroll
@@ -467,45 +484,54 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                                 bool ok = t < t1 && t <= lim[rb];
                                 if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
                                 keep |= ok ? 1 << (4 * hf + i) : 0;
-                                sc[hf][i] = ok ? sc[hf][i] : -INFINITY;
+                                sca[rb][hf][i] = ok ? sca[rb][hf][i] : -INFINITY;
                             }
                         }
+                        keep_rb[rb] = keep;
                         keep_any |= keep;
                     }
-                    float mx = fmax3_raw(fmax3_raw(sc[0][0], sc[0][1], sc[0][2]),
-                                         fmax3_raw(sc[0][3], sc[1][0], sc[1][1]), fmax_raw(sc[1][2], sc[1][3]));
-                    mx = max4_raw(mx) * a.scale_log2;
-                    // move the reference max only when the row's max passes it by
-                    // more than the slack (a row with nothing kept so far keeps
-                    // (m, l, o) = (-inf, 0, 0))
-                    const bool mv = mx > m2[rb] + kRescaleSlack;
+                    const f32x4_t s0 = sca[rb][0], s1 = sca[rb][1];
+                    lmx[rb] = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) *
+                              a.scale_log2;
+                    pass |= lmx[rb] > thr[rb];
+                }
+                return __builtin_amdgcn_ballot_w64(pass) != 0;
+            };
+            const bool moved = full ? scan(std::true_type{}) : scan(std::false_type{});
+            if (moved) {
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float mx = max4(lmx[rb]);
+                    const bool mv = mx > thr[rb];
                     const float mn = mv ? mx : m2[rb];
-                    alpha[rb] = mv ? exp2_fast(m2[rb] - mn) : 1.f;
-                    grow |= mv;
+                    const float alpha = mv ? exp2_fast(m2[rb] - mn) : 1.f;
                     m2[rb] = mn;
+                    thr[rb] = mn + kRescaleSlack;
+    #pragma unroll
+                    for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha;
+                    lacc[rb] *= alpha;
+                }
+            }
+            auto weights = [&](auto full_c) {
+                constexpr bool FULL = decltype(full_c)::value;
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
                     float p[8];
     #pragma unroll
                     for (int hf = 0; hf < 2; ++hf) {
     #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float e = exp2_fast(fmaf(sc[hf][i], a.scale_log2, -mn));
-                            p[4 * hf + i] = FULL || ((keep >> (4 * hf + i)) & 1) ? e : 0.f;
+                            const float e = exp2_fast(fmaf(sca[rb][hf][i], a.scale_log2, -m2[rb]));
+                            p[4 * hf + i] = FULL || ((keep_rb[rb] >> (4 * hf + i)) & 1) ? e : 0.f;
                         }
                     }
                     pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
                                    pack_bf16(p[6], p[7])};
                 }
             };
-            if (full) softmax(std::true_type{});
-            else softmax(std::false_type{});
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-    #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-    #pragma unroll
-                    for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
-                    lacc[rb] *= alpha[rb];
-                }
-            }
+            if (full) weights(std::true_type{});
+            else weights(std::false_type{});
             // tokens no row keeps get V = 0 (with a mask they may hold anything)
             uint32_t vkeep = 0xffffffffu;
             if constexpr (MASK) {
@@ -585,6 +611,8 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             // every wave is past step st - 1: its stage takes step st + 2
             if (st + 2 < nst) issue(st + 2);
             if (have) compute(st);
+            // the page ids of the step the next iteration issues
+            if (P16 && st + 3 < nst && t0 + 32 * (st + 4) <= t1) prefetch(st + 3);
         }
         // every wave done with the ring before the next item's loads
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
