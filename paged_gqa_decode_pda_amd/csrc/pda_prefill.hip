@@ -306,13 +306,20 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         const int t1 = min(min(t0 + span, P), lim_g + 1);
         const int nst = t1 > t0 ? (t1 - t0 + 31) >> 5 : 0;
 
-        float m2[RB], thr[RB];   // the row's reference max (log2 units) and m2 + slack
-        f32x4_t lacc[RB];        // the row's weight sum (all four elements)
+        // Online-softmax state per row block: the reference max m2 (log2
+        // units), the threshold thr = m2 + slack, the offset the weights are
+        // taken against (mw: m2, or 0 while the row has kept nothing, so that
+        // its -inf scores still give weight 0), the pending rescale factor,
+        // the weight sum (every element of lacc) and O.
+        float m2[RB], thr[RB], mw[RB], alpha[RB];
+        f32x4_t lacc[RB];
         f32x4_t acc[RB][NDB];
     #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             m2[rb] = -INFINITY;
             thr[rb] = -INFINITY;
+            mw[rb] = 0.f;
+            alpha[rb] = 1.f;
             lacc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     #pragma unroll
             for (int n = 0; n < NDB; ++n) acc[rb][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -320,8 +327,6 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
 
         const int32_t *brow = a.blocks + (int64_t)s * a.cap;
         const int64_t gk = (int64_t)g * a.kvh;
-        int cb = t0 / a.bs;   // first page of the page-id window
-        int bidvec = brow[min(cb + lane, a.cap - 1)];
         // This wave's share of a step's loads: instructions j = w + 4 i.  The
         // first NKI are K instructions (j < 2 NCK): half j / NCK, chunk j %
         // NCK, lane l loading token l % 16 of the half, elements kdc[i] (32
@@ -353,37 +358,45 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             vdc[i] = vd < a.D ? vd : 0;
             vob[i] = 2u * (uint32_t)((row - 16 * vhf[i]) * (int)a.tok + vdc[i]);
         }
-        // Element offset of token t's row (kv head g); t must be listed.
-        auto row_of = [&](int t) -> int64_t {
+
+        // Steps that address rows one by one (a half crossing a page, or the
+        // partial last step) take page ids from a 64-page window held one id
+        // per lane.  The K loads run two steps ahead of the V loads, so each
+        // has its own window; a window moves forward only (steps come in
+        // order) and waits for its load where it moves.
+        int cbk = t0 / a.bs, cbv = cbk;   // first page of each window
+        int bidk = brow[min(cbk + lane, a.cap - 1)];
+        int bidv = bidk;
+        auto window_for = [&](int st, int &cb, int &bidvec) __attribute__((always_inline)) {
+            const int tb = t0 + 32 * st;
+            const int last = min(tb + 31, t1 - 1);
+            if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {
+                cb = page_of((uint32_t)tb, a.bs_magic);
+                bidvec = brow[min(cb + lane, a.cap - 1)];
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+        };
+        // element offset of token t's row (kv head g); t must be listed and
+        // inside the window
+        auto row_in = [&](int t, int bidvec, int cb) __attribute__((always_inline)) -> int64_t {
             const int pg = page_of((uint32_t)t, a.bs_magic);
             const int bid = __shfl(bidvec, pg - cb, 64);
             return (int64_t)bid * a.blk + gk + (int64_t)(t - pg * a.bs) * a.tok;
         };
 
-        // The page-id window must cover step st's pages before the first load of
-        // that step is addressed.
-        auto window_for = [&](int st) {
-            const int tb = t0 + 32 * st;
-            const int last = min(tb + 31, t1 - 1);
-            if (page_of((uint32_t)last, a.bs_magic) - cb >= 64) {   // move the window
-                cb = page_of((uint32_t)tb, a.bs_magic);
-                bidvec = brow[min(cb + lane, a.cap - 1)];
-                // wait here, so that the path without a move carries no wait
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            }
-        };
         // Steps whose halves each lie inside one page address their loads
         // from the halves' first rows.  Their page ids come through the
         // scalar cache (the block table is read-only here, so the constant
-        // address space may serve it), fetched at the end of the step before
-        // the one that issues them: the fetch is in flight through the
-        // barrier wait, not in front of the LDS reads, which wait for every
-        // scalar load too.  No vector-to-scalar move or page-id window is on
-        // this path.
+        // address space may serve it), fetched at the end of the iteration
+        // before the one that issues the step's K: the fetch is in flight
+        // through the barrier wait, not in front of the LDS reads, which wait
+        // for every scalar load too.  The half bases are computed once, for
+        // the K loads, and kept for the V loads two iterations later in a
+        // three-step queue (hq[0]: the oldest).
         const __attribute__((address_space(4))) int32_t *brow_c =
             (const __attribute__((address_space(4))) int32_t *)brow;
         int pf_st = -1, pf_b[2] = {0, 0}, pf_r[2] = {0, 0};   // prefetched: step, page ids, rows in page
-        auto prefetch = [&](int st) {
+        auto prefetch = [&](int st) __attribute__((always_inline)) {
             const int tb = t0 + 32 * st;
     #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
@@ -396,60 +409,94 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // first element of each half's first row (kv head g); the strides are
         // below 2^32 and in-page offsets below 2^31 (checked by the host), so
         // 32-bit factors suffice
-        int64_t hb[2] = {0, 0};
+        int64_t hq[3][2] = {{0, 0}, {0, 0}, {0, 0}};
         const uint32_t blk32 = (uint32_t)a.blk, tok32 = (uint32_t)a.tok;
-        auto bases = [&](int st) {
-            if (pf_st != st) prefetch(st);
+        auto uniform_step = [&](int st) __attribute__((always_inline)) { return P16 && t0 + 32 * st + 32 <= t1; };
+        auto shift_q = [&]() __attribute__((always_inline)) {
     #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-                hb[hf] = (int64_t)((uint64_t)(uint32_t)pf_b[hf] * blk32 + (uint32_t)pf_r[hf] * tok32) + gk;
+            for (int hf = 0; hf < 2; ++hf) {
+                hq[0][hf] = hq[1][hf];
+                hq[1][hf] = hq[2][hf];
+            }
         };
-        // This wave's share of step st's loads into stage st % kPfStages.
-        auto issue = [&](int st) {
-            const int tb = t0 + 32 * st;
-            lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
-            if (P16 && tb + 32 <= t1) {   // both halves whole pages' rows: uniform bases
-                bases(st);
+        // This wave's share of step j's K loads into stage j % kPfStages (its
+        // half bases into hq[2]), and of step j's V loads (its half bases in
+        // hq[0]).
+        auto issue_k = [&](int j) __attribute__((always_inline)) {
+            lds_u8_t *stg = ring_lds + (j % kPfStages) * SG::BYTES;
+            if (uniform_step(j)) {
+                if (pf_st != j) prefetch(j);
+    #pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    hq[2][hf] = (int64_t)((uint64_t)(uint32_t)pf_b[hf] * blk32 + (uint32_t)pf_r[hf] * tok32) + gk;
     #pragma unroll
                 for (int i = 0; i < NKI; ++i)
-                    ld16_lds(reinterpret_cast<const char *>(a.k + (khf[i] ? hb[1] : hb[0])) + kob[i],
+                    ld16_lds(reinterpret_cast<const char *>(a.k + (khf[i] ? hq[2][1] : hq[2][0])) + kob[i],
                              stg + 1024 * (w + kPfWaves * i));
-    #pragma unroll
-                for (int i = 0; i < NVI; ++i)
-                    ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hb[1] : hb[0])) + vob[i],
-                             stg + SG::KBYTES + 1024 * (w + kPfWaves * i));
             } else {   // rows past t1 read a listed row (weight 0)
-                window_for(st);
+                const int tb = t0 + 32 * j;
+                window_for(j, cbk, bidk);
     #pragma unroll
                 for (int i = 0; i < NKI; ++i) {
                     const int t = min(tb + 16 * khf[i] + col, t1 - 1);
-                    ld16_lds(a.k + row_of(t) + kdc[i], stg + 1024 * (w + kPfWaves * i));
-                }
-    #pragma unroll
-                for (int i = 0; i < NVI; ++i) {
-                    const int t = min(tb + vtok[i], t1 - 1);
-                    ld16_lds(a.v + row_of(t) + vdc[i], stg + SG::KBYTES + 1024 * (w + kPfWaves * i));
+                    ld16_lds(a.k + row_in(t, bidk, cbk) + kdc[i], stg + 1024 * (w + kPfWaves * i));
                 }
             }
         };
+        auto issue_v = [&](int j) __attribute__((always_inline)) {
+            lds_u8_t *stg = ring_lds + (j % kPfStages) * SG::BYTES + SG::KBYTES;
+            if (uniform_step(j)) {
+    #pragma unroll
+                for (int i = 0; i < NVI; ++i)
+                    ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hq[0][1] : hq[0][0])) + vob[i],
+                             stg + 1024 * (w + kPfWaves * i));
+            } else {
+                const int tb = t0 + 32 * j;
+                window_for(j, cbv, bidv);
+    #pragma unroll
+                for (int i = 0; i < NVI; ++i) {
+                    const int t = min(tb + vtok[i], t1 - 1);
+                    ld16_lds(a.v + row_in(t, bidv, cbv) + vdc[i], stg + 1024 * (w + kPfWaves * i));
+                }
+            }
+        };
+        // Wait until at most nk steps' K loads and nv steps' V loads of this
+        // wave are in flight (loads complete in order).
+        auto wait_loads = [&](int nk, int nv) __attribute__((always_inline)) {
+            const int n = nk * NKI + nv * NVI;
+            if (n == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            else if (n == NKI) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NKI));
+            else if (n == NVI) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NVI));
+            else if (n == NKI + NVI) __builtin_amdgcn_s_waitcnt(vmcnt_wait(NKI + NVI));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_wait(2 * NKI + NVI));
+        };
+        auto barrier = [&]() __attribute__((always_inline)) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_barrier();
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        };
 
-        auto compute = [&](int st) {
-            const int tb = t0 + 32 * st;
-            const lds_u8_t *stg = ring_lds + (st % kPfStages) * SG::BYTES;
-            // K of the step from the stage, in the product's operand layout
-            u32x4 kflat[2 * NCK];   // [half * NCK + chunk]
-            lds_read_k(kflat, stg + 16 * lane);
-            // scores, transposed: lane -> row col, tokens 16 hf + 4 qd + i.  A
-            // step inside every row's range (and the split's) keeps all tokens
-            // and takes the path without per-token tests.
-            const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
-            u32x4 pb[RB];
-            int keep_any = 0;   // bit 4 hf + i: some row keeps token 16 hf + 4 qd + i
-            int keep_rb[RB];    // the same for each row block's row
-            float lmx[RB];   // this lane's maximum scaled score per row block
-            // every row block's score products, then the next step's K into the
-            // same registers
-            f32x4_t sca[RB][2];
+        // The step loop is pipelined across steps: iteration st computes
+        // P.V of step st - 1 and the scores of step st + 1 on the matrix
+        // cores and the weights of step st on the vector ALU, all independent
+        // of one another, so each wave interleaves the two kinds of work (a
+        // wave's matrix-core and vector work overlap; two waves' on one SIMD
+        // mostly do not).  K runs three steps ahead of the compute and V one:
+        // iteration st issues K(st + 3) and V(st + 1) and reads K(st + 1) and
+        // V(st - 1), all from stage (step % 3) of the K and V rings.
+        f32x4_t s_cur[RB][2], s_nxt[RB][2];   // scores (transposed) of steps st and st + 1
+        u32x4 pb_prev[RB], pb_cur[RB];        // bf16 weights of steps st - 1 and st
+        int kp_prev = 0xff, kp_cur = 0xff, kp_nxt = 0xff;   // with a mask: tokens some row keeps
+        bool resc = false;                    // a rescale by alpha is pending
+    #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            s_cur[rb][0] = s_cur[rb][1] = s_nxt[rb][0] = s_nxt[rb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            pb_prev[rb] = pb_cur[rb] = u32x4{0, 0, 0, 0};
+        }
+
+        // scores of step st from its K (already in registers), transposed:
+        // lane -> row col, tokens 16 hf + 4 qd + i
+        auto scores = [&](f32x4_t (&sc)[RB][2], const u32x4 (&kf)[2 * NCK]) __attribute__((always_inline)) {
     #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
     #pragma unroll
@@ -457,105 +504,106 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                     f32x4_t x = {0.f, 0.f, 0.f, 0.f};
     #pragma unroll
                     for (int c = 0; c < NCK; ++c)
-                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kflat[hf * NCK + c]),
+                        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[hf * NCK + c]),
                                                                     __builtin_bit_cast(bf16x8_t, qb[rb][c]), x,
                                                                     0, 0, 0);
-                    sca[rb][hf] = x;
+                    sc[rb][hf] = x;
                 }
             }
-            // Scores to weights.  The reference max of a row moves only when
-            // the row's max passes it by more than the slack (a row with
-            // nothing kept so far keeps (m, l, o) = (-inf, 0, 0)); while no
-            // lane of the wave passes its rows' threshold, no row moves and
-            // the cross-lane maxima are skipped.
-            auto scan = [&](auto full_c) -> bool {
-                constexpr bool FULL = decltype(full_c)::value;
-                bool pass = false;
+        };
+        // The scan of step st's scores: tokens a row does not keep get -inf
+        // (a step inside every row's range, and the split's, keeps all and
+        // skips the tests); each lane's maximum scaled score against its rows'
+        // thresholds.  The reference max of a row moves only when the row's
+        // max passes it by more than the slack (a row with nothing kept so far
+        // keeps (m, l, o) = (-inf, 0, 0)); while no lane of the wave passes,
+        // no row moves and the cross-lane maxima are skipped.  A move takes
+        // effect for the weights of step st; the rescale of O and l by alpha
+        // waits for P.V of step st - 1 (resc).
+        auto scan = [&](int st, f32x4_t (&sc)[RB][2], int &keep_any) __attribute__((always_inline)) {
+            const int tb = t0 + 32 * st;
+            const bool full = !MASK && tb + 32 <= t1 && tb + 31 <= lim_min;
+            keep_any = 0xff;
+            if (!full) {
+                int ka = 0;
     #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    // keep bit 4 hf + i: the row keeps token tb + 16 hf + 4 qd + i
-                    if constexpr (!FULL) {
-                        int keep = 0;
     #pragma unroll
-                        for (int hf = 0; hf < 2; ++hf) {
+                    for (int hf = 0; hf < 2; ++hf) {
     #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int t = tb + 16 * hf + 4 * qd + i;
-                                bool ok = t < t1 && t <= lim[rb];
-                                if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
-                                keep |= ok ? 1 << (4 * hf + i) : 0;
-                                sca[rb][hf][i] = ok ? sca[rb][hf][i] : -INFINITY;
-                            }
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = tb + 16 * hf + 4 * qd + i;
+                            bool ok = t < t1 && t <= lim[rb];
+                            if constexpr (MASK) ok = ok && mrow[rb][t] != 0;
+                            ka |= ok ? 1 << (4 * hf + i) : 0;
+                            sc[rb][hf][i] = ok ? sc[rb][hf][i] : -INFINITY;
                         }
-                        keep_rb[rb] = keep;
-                        keep_any |= keep;
                     }
-                    const f32x4_t s0 = sca[rb][0], s1 = sca[rb][1];
-                    lmx[rb] = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
-                                    fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) *
-                              a.scale_log2;
-                    pass |= lmx[rb] > thr[rb];
                 }
-                return __builtin_amdgcn_ballot_w64(pass) != 0;
-            };
-            const bool moved = full ? scan(std::true_type{}) : scan(std::false_type{});
-            if (moved) {
+                keep_any = or16(ka);
+            }
+            float lmx[RB];
+            bool pass = false;
+    #pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const f32x4_t s0 = sc[rb][0], s1 = sc[rb][1];
+                lmx[rb] = fmaxf(fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3])),
+                                fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3]))) *
+                          a.scale_log2;
+                pass |= lmx[rb] > thr[rb];
+            }
+            if (__builtin_amdgcn_ballot_w64(pass) != 0) {
     #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     const float mx = max4(lmx[rb]);
                     const bool mv = mx > thr[rb];
                     const float mn = mv ? mx : m2[rb];
-                    const float alpha = mv ? exp2_fast(m2[rb] - mn) : 1.f;
+                    alpha[rb] = mv ? exp2_fast(m2[rb] - mn) : 1.f;
                     m2[rb] = mn;
                     thr[rb] = mn + kRescaleSlack;
-    #pragma unroll
-                    for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha;
-                    lacc[rb] *= alpha;
+                    mw[rb] = mn == -INFINITY ? 0.f : mn;
                 }
+                resc = true;
             }
-            auto weights = [&](auto full_c) {
-                constexpr bool FULL = decltype(full_c)::value;
+        };
+        // bf16 weights of step st (masked scores are -inf: weight 0), for
+        // the (row block, half) pairs k0 .. k1 - 1 of the 2 RB
+        auto weights = [&](const f32x4_t (&sc)[RB][2], u32x4 (&pb)[RB], auto k0c, auto k1c) __attribute__((always_inline)) {
+            constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
     #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                    float p[8];
+            for (int k = K0; k < K1; ++k) {
+                const int rb = k >> 1, hf = k & 1;
+                float p[4];
     #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-    #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float e = exp2_fast(fmaf(sca[rb][hf][i], a.scale_log2, -m2[rb]));
-                            p[4 * hf + i] = FULL || ((keep_rb[rb] >> (4 * hf + i)) & 1) ? e : 0.f;
-                        }
-                    }
-                    pb[rb] = u32x4{pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]), pack_bf16(p[4], p[5]),
-                                   pack_bf16(p[6], p[7])};
-                }
-            };
-            if (full) weights(std::true_type{});
-            else weights(std::false_type{});
-            // tokens no row keeps get V = 0 (with a mask they may hold anything)
-            uint32_t vkeep = 0xffffffffu;
-            if constexpr (MASK) {
-                keep_any = or16(keep_any);
-                if (__builtin_amdgcn_ballot_w64(keep_any != 0xff) != 0)
-                    vkeep = 0;   // decided per element below
+                for (int i = 0; i < 4; ++i) p[i] = exp2_fast(fmaf(sc[rb][hf][i], a.scale_log2, -mw[rb]));
+                pb[rb][2 * hf] = pack_bf16(p[0], p[1]);
+                pb[rb][2 * hf + 1] = pack_bf16(p[2], p[3]);
+                // computed here, beside the matrix-core work of the phase (the
+                // compiler would otherwise sink it to the end of the iteration)
+                asm volatile("" ::"v"(pb[rb][2 * hf]), "v"(pb[rb][2 * hf + 1]));
             }
-            wave_lds_sync();
-            // P.V: A = V^T block n, lane (qd, col) holding column 16 n + col of
-            // tokens 4 qd .. 4 qd + 3 of each half.  A transposing LDS read
-            // (ds_read_b64_tr_b16) gives lane i of each 16-lane group element
-            // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3; so
-            // lane (qd, c) points at row 4 qd + c / 4 (of each half), elements
-            // 16 n + 4 (c % 4) .. + 3.
-            // l: the same product with a block of ones for V^T sums each
-            // row's weights exactly as rounded for P.V (every element of
-            // lacc holds the row's sum)
+        };
+        // P.V of the step in ring stage stg with weights pb (keep_any: with a
+        // mask, the tokens some row keeps; the others' V may hold anything
+        // and is zeroed).  l: the same product with a block of ones for V^T
+        // sums each row's weights exactly as rounded for P.V.
+        auto pv = [&](const lds_u8_t *stg, const u32x4 (&pb)[RB], int keep_any) __attribute__((always_inline)) {
     #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kOnes),
                                                                    __builtin_bit_cast(bf16x8_t, pb[rb]), lacc[rb],
                                                                    0, 0, 0);
-            // head-dim blocks four at a time: their transposed reads, then
-            // their products
+            uint32_t vkeep = 0xffffffffu;
+            if constexpr (MASK) {
+                if (__builtin_amdgcn_ballot_w64(keep_any != 0xff) != 0) vkeep = 0;   // decided per element
+            }
+            // A = V^T block n, lane (qd, col) holding column 16 n + col of
+            // tokens 4 qd .. 4 qd + 3 of each half.  A transposing LDS read
+            // (ds_read_b64_tr_b16) gives lane i of each 16-lane group element
+            // i % 4 of the 8-byte chunks read by lanes i / 4 + 4 j, j = 0..3;
+            // so lane (qd, c) points at row 4 qd + c / 4 (of each half),
+            // elements 16 n + 4 (c % 4) .. + 3.  Head-dim blocks four at a
+            // time: their transposed reads, then their products.
             auto pv4 = [&](auto mc) {
                 constexpr int M = decltype(mc)::value;
                 i16x4_t lo4[4], hi4[4];
@@ -590,34 +638,99 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 pv4(std::integral_constant<int, 2>{});
                 pv4(std::integral_constant<int, 3>{});
             }
-            wave_lds_sync();
+        };
+
+        // Iteration st of the pipeline; PV, NEXT, W: whether step st - 1, st
+        // + 1, st exist (the same in every wave).
+        auto iter = [&](int st, auto pv_c, auto next_c, auto w_c) __attribute__((always_inline)) {
+            constexpr bool PV = decltype(pv_c)::value, NEXT = decltype(next_c)::value, W = decltype(w_c)::value;
+            // this wave's loads of K(st + 1) and V(st - 1) have landed (those
+            // of K(st + 2) and V(st) may still be in flight), then everyone's;
+            // every wave is past iteration st - 1, which read the stages that
+            // K(st + 3) and V(st + 1) take
+            wait_loads(st + 2 < nst ? 1 : 0, st < nst ? 1 : 0);
+            barrier();
+            if (st + 3 < nst) issue_k(st + 3);
+            if (st + 1 < nst) issue_v(st + 1);
+            shift_q();
+            if (have) {
+                // two phases, each pairing matrix-core work with half of the
+                // weights: P.V of step st - 1, then the scores of step st + 1
+                // (the phase boundaries keep the compiler from hoisting the K
+                // read, and with it 2 NCK registers, into the first)
+                constexpr std::integral_constant<int, 0> k0{};
+                constexpr std::integral_constant<int, RB> kh{};
+                constexpr std::integral_constant<int, 2 * RB> k2{};
+                if constexpr (PV) pv(ring_lds + ((st + 2) % kPfStages) * SG::BYTES, pb_prev, kp_prev);
+                if constexpr (W) weights(s_cur, pb_cur, k0, kh);
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NEXT) {
+                    u32x4 kflat[2 * NCK];
+                    lds_read_k(kflat, ring_lds + ((st + 1) % kPfStages) * SG::BYTES + 16 * lane);
+                    scores(s_nxt, kflat);
+                }
+                if constexpr (W) weights(s_cur, pb_cur, kh, k2);
+                __builtin_amdgcn_sched_barrier(0);
+                // the rescale a move at step st asks for, after P.V of step st - 1
+                if (resc) {
+    #pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+    #pragma unroll
+                        for (int n = 0; n < NDB; ++n) acc[rb][n] *= alpha[rb];
+                        lacc[rb] *= alpha[rb];
+                    }
+                    resc = false;
+                }
+                if constexpr (NEXT) scan(st + 1, s_nxt, kp_nxt);
+    #pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    pb_prev[rb] = pb_cur[rb];
+                    s_cur[rb][0] = s_nxt[rb][0];
+                    s_cur[rb][1] = s_nxt[rb][1];
+                }
+                kp_prev = kp_cur;
+                kp_cur = kp_nxt;
+            }
+            // the page ids of the K step the next iteration issues
+            if (st + 4 < nst && uniform_step(st + 4)) prefetch(st + 4);
         };
 
         // the item's q rows and page ids in registers before the ring's loads
         // start (the compiler would otherwise wait for all loads in flight at
         // every use of them)
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        // the ring: steps st + 1 and st + 2 in flight while st is computed
-        if (nst > 0) issue(0);
-        if (nst > 1) issue(1);
-        for (int st = 0; st < nst; ++st) {
-            // this wave's loads of step st have landed (the next step's may
-            // still be in flight; loads complete in order), then everyone's
-            if (st + 1 < nst) __builtin_amdgcn_s_waitcnt(vmcnt_wait(SHARE));
-            else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_barrier();
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            // every wave is past step st - 1: its stage takes step st + 2
-            if (st + 2 < nst) issue(st + 2);
-            if (have) compute(st);
-            // the page ids of the step the next iteration issues
-            if (P16 && st + 3 < nst && t0 + 32 * (st + 4) <= t1) prefetch(st + 3);
+        if (nst > 0) {
+            // K(0), K(1), K(2) and V(0) in flight; wait for K(0)
+            issue_k(0);
+            shift_q();
+            if (1 < nst) issue_k(1);
+            shift_q();
+            if (2 < nst) issue_k(2);
+            issue_v(0);
+            shift_q();
+            wait_loads((1 < nst ? 1 : 0) + (2 < nst ? 1 : 0), 1);
+            barrier();
+            if (have) {
+                u32x4 kflat[2 * NCK];
+                lds_read_k(kflat, ring_lds + 16 * lane);
+                scores(s_cur, kflat);
+                scan(0, s_cur, kp_cur);
+            }
+            if (3 < nst && uniform_step(3)) prefetch(3);
+            const std::true_type T{};
+            const std::false_type F{};
+            if (nst == 1) {
+                iter(0, F, F, T);
+                iter(1, T, F, F);
+            } else {
+                iter(0, F, T, T);
+                for (int st = 1; st < nst - 1; ++st) iter(st, T, T, T);
+                iter(nst - 1, T, F, T);
+                iter(nst, T, F, F);
+            }
         }
         // every wave done with the ring before the next item's loads
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        barrier();
 
         // totals: lane l holds O[row col][16 n + 4 qd + i]
     #pragma unroll
