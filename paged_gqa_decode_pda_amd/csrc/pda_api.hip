@@ -77,10 +77,15 @@ int32_t min_auto_bps(const pda_dims *d) {
 }
 
 int device_cus() {
+    // queried once per device (the count does not change while the process runs)
+    static std::atomic<int> known[64];   // 0: not yet queried
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const bool slot = dev >= 0 && dev < 64;
+    if (slot && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return 256;
+    if (slot) known[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
