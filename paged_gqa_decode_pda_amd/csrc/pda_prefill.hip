@@ -11,7 +11,7 @@
 // With q_len * G query rows per kv head the scores are a dense contraction,
 // so both products run on v_mfma_f32_16x16x32_bf16:
 //   scores, transposed: S^T (16 tokens x 16 rows) = K (A operand, 16 token
-//      rows loaded straight from the pages) x Q^T (B operand, the q rows).
+//      rows from the ring below) x Q^T (B operand, the q rows).
 //      Lane l gets rows l%16 and tokens 4(l/16) + i, i = 0..3, so two
 //      16-token halves leave lane l exactly the 8 weights that the B operand
 //      of the next product needs from row l%16: no transpose of P.
@@ -27,13 +27,17 @@
 // Work items: (sequence, kv split, kv head, group of four row tiles); a
 // workgroup takes one, each of its four waves one row tile (RB row blocks of
 // 16 query rows, rows r = i * G + (h - g G) of kv head g), and they stream
-// the split's tokens in steps of 32 through a three-stage ring in LDS: K and
+// the split's tokens in steps of 32 through three-stage rings in LDS: K and
 // V of a step are loaded once for the four waves, straight from memory into
 // LDS (gfx950's global_load_lds_dwordx4, a quarter of the loads per wave),
-// two steps ahead, and every wave reads them from the ring (K in exactly the
-// product's operand layout).  One barrier per step: behind it every wave's
-// loads of the step have landed and every wave is done with the stage that
-// the next loads overwrite.  Units (sequence, kv split, kv head) are
+// and every wave reads them from the rings (K in exactly the product's
+// operand layout).  The step loop is pipelined across steps: iteration st
+// computes P.V of step st - 1 and the scores of step st + 1 on the matrix
+// cores beside the weights of step st on the vector ALU, so each wave
+// interleaves the two kinds of work; K is loaded three steps ahead and V
+// one.  One barrier per iteration: behind it every wave's loads that the
+// iteration reads have landed and every wave is done with the stages that
+// the iteration's loads overwrite.  Units (sequence, kv split, kv head) are
 // dealt round-robin to the eight XCDs, longest first when there are few
 // enough (sequence, split) pairs to rank in each workgroup, and a unit's row
 // tiles, which read the same pages, run on consecutive waves of one XCD.
@@ -55,7 +59,6 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) unsigned char lds_u8_t;
 
 // One stage of the ring: a 32-token step's K, [half][chunk] blocks of 64
