@@ -119,6 +119,34 @@ def test_prefill_small_shapes(shape, bps, rpw):
         check(got, ref, case, f"prefill {shape} causal={causal} bps={bps} rpw={rpw}")
 
 
+# Page lists longer than the 64-page windows that steps addressing rows one by
+# one read their page ids from (the K loads run two steps ahead of the V
+# loads, each with its own window): block sizes that are not a multiple of 16
+# take that path on every step, and a long 16-token-page context takes it on
+# its partial last step only, after every earlier step skipped the window.
+LONG_LISTS = [
+    # S, Q, Hq, Hkv, D, bs, contexts, layout
+    (1, 6, 4, 2, 64, 1, [150], "paged"),
+    (1, 3, 8, 2, 128, 4, [400], "scratch"),
+    (1, 4, 8, 8, 256, 2, [300], "paged"),
+    (2, 5, 8, 2, 128, 16, [2100, 40], "paged"),
+]
+
+
+@pytest.mark.parametrize("shape", LONG_LISTS, ids=_ids)
+@pytest.mark.parametrize("rpw", [0, 64])
+def test_prefill_long_page_lists(shape, rpw):
+    S, Q, Hq, Hkv, D, bs, ctx, layout = shape
+    announce("prefill long page list", shape, "rows/wave", rpw)
+    rng = np.random.Generator(np.random.PCG64(hash((S, Q, Hq, Hkv, D, bs, 7)) % (1 << 32)))
+    case = prefill_case(rng, S, Q, Hq, Hkv, D, bs, ctx, layout=layout)
+    dev = Device(case)
+    for causal in (True, False):
+        got = out_to_f64(run_prefill(dev, case.qc, causal=causal, bps=0, rpw=rpw))
+        ref = oracle_prefill(case, causal=causal)["out"]
+        check(got, ref, case, f"prefill long list {shape} causal={causal} rpw={rpw}")
+
+
 @pytest.mark.parametrize("order", ["ranked", "unranked"])
 def test_prefill_multi_round_work_orders(order):
     """Grids that take several rounds of the CUs: with at most 256 (sequence,
