@@ -34,7 +34,7 @@
 // operand layout).  The step loop is pipelined across steps: iteration st
 // computes P.V of step st - 1 and the scores of step st + 1 on the matrix
 // cores beside the weights of step st on the vector ALU, so each wave
-// interleaves the two kinds of work; K is loaded three steps ahead and V
+// interleaves the two kinds of work; K is loaded two steps ahead and V
 // one.  One barrier per iteration: behind it every wave's loads that the
 // iteration reads have landed and every wave is done with the stages that
 // the iteration's loads overwrite.  Units (sequence, kv split, kv head) are
@@ -394,8 +394,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // before the one that issues the step's K: the fetch is in flight
         // through the barrier wait, not in front of the LDS reads, which wait
         // for every scalar load too.  The half bases are computed once, for
-        // the K loads, and kept for the V loads two iterations later in a
-        // three-step queue (hq[0]: the oldest).
+        // the K loads, and kept for the V loads one iteration later.
         const __attribute__((address_space(4))) int32_t *brow_c =
             (const __attribute__((address_space(4))) int32_t *)brow;
         int pf_st = -1, pf_b[2] = {0, 0}, pf_r[2] = {0, 0};   // prefetched: step, page ids, rows in page
@@ -412,29 +411,25 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // first element of each half's first row (kv head g); the strides are
         // below 2^32 and in-page offsets below 2^31 (checked by the host), so
         // 32-bit factors suffice
-        int64_t hq[3][2] = {{0, 0}, {0, 0}, {0, 0}};
+        int64_t hk[2] = {0, 0}, hv[2] = {0, 0};   // of the K step last issued, of the next V step
         const uint32_t blk32 = (uint32_t)a.blk, tok32 = (uint32_t)a.tok;
         auto uniform_step = [&](int st) __attribute__((always_inline)) { return P16 && t0 + 32 * st + 32 <= t1; };
         auto shift_q = [&]() __attribute__((always_inline)) {
-    #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                hq[0][hf] = hq[1][hf];
-                hq[1][hf] = hq[2][hf];
-            }
+            hv[0] = hk[0];
+            hv[1] = hk[1];
         };
         // This wave's share of step j's K loads into stage j % kPfStages (its
-        // half bases into hq[2]), and of step j's V loads (its half bases in
-        // hq[0]).
+        // half bases into hk), and of step j's V loads (its half bases in hv).
         auto issue_k = [&](int j) __attribute__((always_inline)) {
             lds_u8_t *stg = ring_lds + (j % kPfStages) * SG::BYTES;
             if (uniform_step(j)) {
                 if (pf_st != j) prefetch(j);
     #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
-                    hq[2][hf] = (int64_t)((uint64_t)(uint32_t)pf_b[hf] * blk32 + (uint32_t)pf_r[hf] * tok32) + gk;
+                    hk[hf] = (int64_t)((uint64_t)(uint32_t)pf_b[hf] * blk32 + (uint32_t)pf_r[hf] * tok32) + gk;
     #pragma unroll
                 for (int i = 0; i < NKI; ++i)
-                    ld16_lds(reinterpret_cast<const char *>(a.k + (khf[i] ? hq[2][1] : hq[2][0])) + kob[i],
+                    ld16_lds(reinterpret_cast<const char *>(a.k + (khf[i] ? hk[1] : hk[0])) + kob[i],
                              stg + 1024 * (w + kPfWaves * i));
             } else {   // rows past t1 read a listed row (weight 0)
                 const int tb = t0 + 32 * j;
@@ -451,7 +446,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
             if (uniform_step(j)) {
     #pragma unroll
                 for (int i = 0; i < NVI; ++i)
-                    ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hq[0][1] : hq[0][0])) + vob[i],
+                    ld16_lds(reinterpret_cast<const char *>(a.v + (vhf[i] ? hv[1] : hv[0])) + vob[i],
                              stg + 1024 * (w + kPfWaves * i));
             } else {
                 const int tb = t0 + 32 * j;
@@ -484,9 +479,9 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // cores and the weights of step st on the vector ALU, all independent
         // of one another, so each wave interleaves the two kinds of work (a
         // wave's matrix-core and vector work overlap; two waves' on one SIMD
-        // mostly do not).  K runs three steps ahead of the compute and V one:
-        // iteration st issues K(st + 3) and V(st + 1) and reads K(st + 1) and
-        // V(st - 1), all from stage (step % 3) of the K and V rings.
+        // mostly do not).  Iteration st issues K(st + 2) and V(st + 1) and
+        // reads K(st + 1) and V(st - 1), all from stage (step % 3) of the K
+        // and V rings: K loads have one iteration to land, V loads two.
         f32x4_t s_cur[RB][2], s_nxt[RB][2];   // scores (transposed) of steps st and st + 1
         u32x4 pb_prev[RB], pb_cur[RB];        // bf16 weights of steps st - 1 and st
         int kp_prev = 0xff, kp_cur = 0xff, kp_nxt = 0xff;   // with a mask: tokens some row keeps
@@ -648,12 +643,12 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         auto iter = [&](int st, auto pv_c, auto next_c, auto w_c) __attribute__((always_inline)) {
             constexpr bool PV = decltype(pv_c)::value, NEXT = decltype(next_c)::value, W = decltype(w_c)::value;
             // this wave's loads of K(st + 1) and V(st - 1) have landed (those
-            // of K(st + 2) and V(st) may still be in flight), then everyone's;
-            // every wave is past iteration st - 1, which read the stages that
-            // K(st + 3) and V(st + 1) take
-            wait_loads(st + 2 < nst ? 1 : 0, st < nst ? 1 : 0);
+            // of V(st), issued after K(st + 1), may still be in flight), then
+            // everyone's; every wave is past iteration st - 1, which read the
+            // stages that K(st + 2) and V(st + 1) take
+            wait_loads(0, st < nst ? 1 : 0);
             barrier();
-            if (st + 3 < nst) issue_k(st + 3);
+            if (st + 2 < nst) issue_k(st + 2);
             if (st + 1 < nst) issue_v(st + 1);
             shift_q();
             if (have) {
@@ -701,7 +696,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 __builtin_amdgcn_s_setprio(0);
             }
             // the page ids of the K step the next iteration issues
-            if (st + 4 < nst && uniform_step(st + 4)) prefetch(st + 4);
+            if (st + 3 < nst && uniform_step(st + 3)) prefetch(st + 3);
         };
 
         // the item's q rows and page ids in registers before the ring's loads
@@ -709,15 +704,13 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
         // every use of them)
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         if (nst > 0) {
-            // K(0), K(1), K(2) and V(0) in flight; wait for K(0)
+            // K(0), K(1) and V(0) in flight; wait for K(0)
             issue_k(0);
             shift_q();
             if (1 < nst) issue_k(1);
-            shift_q();
-            if (2 < nst) issue_k(2);
             issue_v(0);
             shift_q();
-            wait_loads((1 < nst ? 1 : 0) + (2 < nst ? 1 : 0), 1);
+            wait_loads(1 < nst ? 1 : 0, 1);
             barrier();
             if (have) {
                 u32x4 kflat[2 * NCK];
@@ -725,7 +718,7 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
                 scores(s_cur, kflat);
                 scan(0, s_cur, kp_cur);
             }
-            if (3 < nst && uniform_step(3)) prefetch(3);
+            if (2 < nst && uniform_step(2)) prefetch(2);
             const std::true_type T{};
             const std::false_type F{};
             if (nst == 1) {
