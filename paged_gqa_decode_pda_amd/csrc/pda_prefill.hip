@@ -187,9 +187,9 @@ __device__ __forceinline__ u32x4 ld16_at(const uint16_t *base, uint32_t byte_off
 }
 
 // Up to 32 rows per wave (head dim up to 128) the registers fit two waves
-// per SIMD (two
-// workgroups per CU), which hide each other's dependency stalls; 64 rows
-// need the whole register file of one wave.
+// per SIMD (two workgroups per CU): while one computes at raised priority
+// the other issues its loads or waits at its barrier; 64 rows need the whole
+// register file of one wave.
 template <int DP, int RB, bool MASK, bool P16, bool LAPS>
 __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) prefill_kernel(const PrefillArgs a) {
     using SG = PfStage<DP>;
@@ -218,8 +218,8 @@ __global__ void __launch_bounds__(kPfThreads, (DP <= 128 && RB <= 2) ? 2 : 1) pr
     // Work assignment.  Hardware workgroup b runs on XCD b % 8 (the grid is
     // a multiple of 8).  Units (sequence, split, kv head), kv head fastest,
     // are dealt round-robin to the XCDs, so each XCD gets an even share of
-    // every sequence; XCD x runs its units in turn, a unit's ntiles row
-    // tiles on consecutive waves (they read the same pages through one L2).
+    // every sequence; XCD x runs its units in turn, a unit's tile groups on
+    // its workgroups (they read the same pages through one L2).
     // When the workgroups take more than one round of the CUs and there are
     // at most kPfSortPairs (sequence, split) pairs, the units are taken
     // longest first, so the launch ends with short work.
