@@ -112,8 +112,8 @@ struct MItem {
 // value the claim saw; a claim that loses that race to another claim of the
 // launch counts on the restarted word.  Counts within a launch are therefore
 // 0, 1, 2, ... whatever the word held before the launch.
-__device__ __forceinline__ uint32_t epoch_claim(unsigned long long *p, uint32_t epoch) {
-    unsigned long long v = __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// epoch_claim_after takes over from a fetch-and-add of 1 that returned v.
+__device__ __forceinline__ uint32_t epoch_claim_after(unsigned long long *p, uint32_t epoch, unsigned long long v) {
     for (;;) {
         if ((uint32_t)(v >> 32) == epoch) return (uint32_t)v;
         unsigned long long cur = v + 1;   // the word right after this claim's add
@@ -128,6 +128,9 @@ __device__ __forceinline__ uint32_t epoch_claim(unsigned long long *p, uint32_t 
         }
         v = __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+__device__ __forceinline__ uint32_t epoch_claim(unsigned long long *p, uint32_t epoch) {
+    return epoch_claim_after(p, epoch, __hip_atomic_fetch_add(p, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Restarts a counter at this launch's epoch with count 0 unless it already
@@ -714,14 +717,20 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             k.obo = (uint32_t)(((int64_t)k.h * a.nsplit * a.D + k.d) * 4);
             return k;
         };
-        auto store = [&](const Chunk &k, const f32x4_m &ov) {
+        // a tile's state chunk (read before the merge's arithmetic, so that
+        // its load travels with the partials')
+        auto state_chunk = [&](const Chunk &k) {
+            f32x4_m st = {0.f, 0.f, 0.f, 0.f};
+            if (TILE && k.ok) st = *reinterpret_cast<const f32x4_m *>(a.o + (row0 + k.h) * a.D + k.d);
+            return st;
+        };
+        auto store = [&](const Chunk &k, const f32x4_m &ov, const f32x4_m &st) {
             if (!k.ok) return;
             const int64_t r = row0 + k.h;
             const float L = lsm[k.h];
             if (TILE) {
                 const float fs = fsm[k.h];
                 float *po = a.o + r * a.D + k.d;
-                const f32x4_m st = *reinterpret_cast<const f32x4_m *>(po);
                 *reinterpret_cast<f32x4_m *>(po) = fs > 0.f ? st * fs + ov : ov;
             } else {
                 u32x2 packed = {0u, 0u};
@@ -732,10 +741,14 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 *reinterpret_cast<u32x2 *>(a.out + r * a.D + k.d) = packed;
             }
         };
-        float ls_st = 0.f, ms_st = -INFINITY;
-        if (TILE && hok) {
-            ls_st = a.l[row0 + hh];
-            ms_st = a.m[row0 + hh] * kLog2e;
+        // a tile's state (l, m) of head hh (read for every lane, used only
+        // where hok: no branch, and no arithmetic on it before the merge's
+        // other loads are issued)
+        float ls_st = 0.f, ms_raw = 0.f;
+        if (TILE) {
+            const int64_t rr = row0 + (hok ? hh : 0);
+            ls_st = a.l[rr];
+            ms_raw = a.m[rr];
         }
 
         if (nslot <= 64 && nslot <= R * lph) {
@@ -757,6 +770,12 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 x0[u] = ld_dev4b(urs, k0.obo + jo);
                 x1[u] = ld_dev4b(urs, k1.obo + jo);
             }
+            const f32x4_m s0 = state_chunk(k0), s1 = state_chunk(k1);
+            // every load above issued before the first wait (the scheduler
+            // would otherwise start the arithmetic on the pairs, and wait for
+            // them, before issuing the o chunks)
+            __builtin_amdgcn_sched_barrier(0);
+            const float ms_st = ms_raw * kLog2e;
             // 2. each head's maximum over the slots holding tokens (and the
             // state), the weights into LDS, L
             float mx = -INFINITY;
@@ -802,8 +821,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                         o1 += (in ? wl[c1.h * 64 + jj] : 0.f) * x1[u];
                     }
                 }
-                store(c0, o0);
-                store(c1, o1);
+                store(c0, o0, p0 == 0 ? s0 : state_chunk(c0));
+                store(c1, o1, p0 == 0 ? s1 : state_chunk(c1));
             }
             if (TILE && hok && jl == 0) {
                 const float L = lsm[hh];
@@ -816,6 +835,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
 
         // More pairs than registers: the same, the pairs read again per chunk
         // of 64 slots and per pass.
+        const float ms_st = ms_raw * kLog2e;
         // 1. each head's maximum over the slots holding tokens (and the state)
         float mx = -INFINITY;
 #pragma unroll 4
@@ -869,8 +889,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                 if (hok && jl == 0) lsm[hh] = TILE ? fmaf(ls_st, ls_st > 0.f ? fsm[hh] : 0.f, lacc) : lacc;
                 wave_lds_sync();
             }
-            store(c0, o0);
-            store(c1, o1);
+            store(c0, o0, state_chunk(c0));
+            store(c1, o1, state_chunk(c1));
         }
         if (TILE && hok && jl == 0) {
             const float L = lsm[hh];
@@ -978,7 +998,13 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         const int nr = (cur.ng + NBUF - 1) / NBUF;
         const bool staged = nr >= 3;
         const int rA = staged ? nr - 3 : -1, rB = staged ? nr - 2 : -1;
-        int grabbed = 0, it_next = nitems, cnt_raw = 0, lv_raw = 0;
+        // Staged items claim the next item with one atomic at round rA and
+        // prefetch it at round rB; a claim that finds another launch's epoch
+        // (rare: the counter is restarted at the launch's start) is completed
+        // after the rounds.
+        unsigned long long claim_raw = 0ull;   // lane 0: the work counter before this wave's add
+        bool fetched = false;
+        int it_next = nitems, cnt_raw = 0, lv_raw = 0;
         nxt.kind = 2;
         if (!staged) {
             it_next = claim_next();
@@ -992,21 +1018,47 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             pw_hi = pn_hi;
             pw_lo = pn_lo;
         }
-        int n = 0;
-        for (int r = 0; r < nr - 1; ++r, n += NBUF) {
-            if (r == rB) {
-                it_next = nwaves + readlane(grabbed, 0);
-                locate(it_next, nxt);
-                fetch(nxt, cnt_raw, lv_raw);
-            }
-            if (r == rA) grabbed = lane == 0 ? (int)epoch_claim(a.work, a.epoch) : 0;
+        // One round: NBUF groups, each issued NBUF - 1 groups ahead of its
+        // step.
+        auto round = [&](int n) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < NBUF; ++j) {
                 issue(cur, n + j + NBUF - 1, rb[(j + NBUF - 1) % NBUF]);
                 if (n + j < cur.ng) step(cur, rb[j], rb[(j + 1) % NBUF], n + j);
             }
+        };
+        // The rounds before rA in a loop of their own, rounds rA (the claim)
+        // and rB (the next item's fetch) written out after it: with the
+        // work-counter atomic inside the loop's body, the compiler drained
+        // every load in flight once per round (measured: wide-head and small
+        // batches 1.5-3 % faster without that drain).
+        int n = 0;
+        for (int r = 0; r < (staged ? rA : nr - 1); ++r, n += NBUF) round(n);
+        if (staged) {
+            claim_raw = lane == 0 ? __hip_atomic_fetch_add(a.work, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : 0ull;
+            round(n);
+            n += NBUF;
+            const uint32_t chi = (uint32_t)readlane((int)(uint32_t)(claim_raw >> 32), 0);
+            if (chi == a.epoch) {
+                it_next = nwaves + readlane((int)(uint32_t)claim_raw, 0);
+                locate(it_next, nxt);
+                fetch(nxt, cnt_raw, lv_raw);
+                fetched = true;
+            }
+            round(n);
+            n += NBUF;
         }
-        if (staged) resolve(nxt, cnt_raw, lv_raw);
+        if (staged) {
+            if (!fetched) {
+                const int g = lane == 0 ? (int)epoch_claim_after(a.work, a.epoch, claim_raw) : 0;
+                it_next = nwaves + readlane(g, 0);
+                locate(it_next, nxt);
+                fetch(nxt, cnt_raw, lv_raw);
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+            resolve(nxt, cnt_raw, lv_raw);
+        }
         issue(cur, n + NBUF - 1, rb[NBUF - 1]);
         if (n < cur.ng) step(cur, rb[0], rb[1], n);
 #pragma unroll
