@@ -287,9 +287,11 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                     ns = 0;
                 }
             }
+            // inclusive scan over the wave's lanes that hold sequences (the
+            // first nsw): offsets below nsw only, the total in lane nsw - 1
+            const int nsw = min(64, a.S - base - 64 * w);
             int xb = nb, xl = nl, xs = ns;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
+            for (int off = 1; off < nsw; off <<= 1) {
                 const int yb = __shfl_up(xb, off, 64);
                 const int yl = __shfl_up(xl, off, 64);
                 const int ys = __shfl_up(xs, off, 64);
@@ -299,7 +301,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
                     xs += ys;
                 }
             }
-            if (lane == 63) {
+            if (lane == (nsw > 0 ? nsw - 1 : 0)) {
                 scan[w] = xb;
                 scan[kMWaves + w] = xl;
                 scan[2 * kMWaves + w] = xs;
