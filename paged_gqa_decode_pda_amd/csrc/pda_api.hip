@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -217,6 +218,10 @@ pda::AttendArgs attend_args(const pda_dims *d, const void *q, const void *k, con
     a.lv_default = lv_default;
     a.prefix_mode = S <= pda::kPrefixMaxSeqs ? 1 : 0;
     a.epoch = next_epoch();
+    // Test knob: without the restart at the launch's start, every counter a
+    // launch finds with another epoch is restarted by its first claim (the
+    // claims' own path, otherwise taken only in a race with the restart).
+    a.restart = std::getenv("PDA_DEBUG_NO_COUNTER_RESTART") ? 0 : 1;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
     char *wsb = static_cast<char *>(ws);
     a.work = reinterpret_cast<unsigned long long *>(wsb);

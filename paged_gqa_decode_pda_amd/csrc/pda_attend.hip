@@ -211,7 +211,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     // waves finishing their first items all at once would otherwise contend
     // for the compare-and-swap that restarts a word found with another
     // launch's epoch.
-    {
+    if (a.restart) {
         const int64_t gsize = (int64_t)gridDim.x * kMThreads;
         const int64_t gtid = (int64_t)blockIdx.x * kMThreads + tid;
         if (gtid == 0) epoch_restart(a.work, a.epoch);

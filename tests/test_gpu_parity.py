@@ -468,6 +468,36 @@ def test_workspace_reuse_across_calls():
                 first[(i, bps)] = bits
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_counters_restarted_by_claims(D, monkeypatch):
+    """With the restart of the counters at the launch's start switched off
+    (the PDA_DEBUG_NO_COUNTER_RESTART test knob), every counter a launch finds
+    holding another epoch is restarted by the launch's first claim on it: the
+    work-item claims (the one made inside a work item's rounds included, whose
+    restart the kernel completes after the rounds) and the arrival counts.
+    Decode and tiled results keep the bits of normal launches, on all-ones
+    (the harness's) and random workspaces, with the default splits (work
+    items long enough to claim inside their rounds) and with short ones."""
+    import torch
+    announce("counters restarted by claims", D)
+    rng = np.random.Generator(np.random.PCG64(61 + D))
+    case = build_case(rng, 5, 8, 2, D, 16, [900, 33, 2600, 0, 4100], cap=320, n_tiles=2)
+    dev = Device(case)
+    refs = {}
+    for bps in (0, 2):
+        refs[bps] = (out_bits(dev.decode(bps=bps)), out_bits(dev.tiled(bps=bps)[1]))
+    monkeypatch.setenv("PDA_DEBUG_NO_COUNTER_RESTART", "1")
+    for bps in (0, 2):
+        for trial in range(2):
+            ws = dev.workspace(bps)
+            if trial == 1:
+                r = np.random.Generator(np.random.PCG64(200 + bps))
+                host = r.integers(0, 1 << 32, size=ws.numel(), dtype=np.uint64).astype(np.uint32)
+                ws.copy_(torch.from_numpy(host.view(np.int32)).to(ws.device))
+            np.testing.assert_array_equal(out_bits(dev.decode(bps=bps, ws=ws)), refs[bps][0])
+        np.testing.assert_array_equal(out_bits(dev.tiled(bps=bps)[1]), refs[bps][1])
+
+
 @pytest.mark.parametrize("fill", ["random", "mid-launch"])
 def test_workspace_any_content(fill):
     """The workspace needs no clearing: random bytes, or counters left as a
