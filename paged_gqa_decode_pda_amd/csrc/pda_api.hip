@@ -587,14 +587,28 @@ pda_status pda_prefill(const pda_dims *dims, int32_t q_len, const void *q, const
     const int dp = padded_dim(dims->head_dim);
     int rb = rows_per_wave / 16;
     const int max_rb = pda::prefill_max_rb(dp, kv_mask != nullptr);
+    const int cus = device_cus();
     if (rb == 0) {   // 16 rows per wave when they cover a kv head's rows, else 32: at 32
                      // rows two waves fit each SIMD (64 rows are left to explicit requests)
         const int64_t rows = (int64_t)q_len * G;
         rb = rows <= 16 ? 1 : 2;
+        if (rb == 2 && dp <= 128) {
+            // ... and 16 when the tile groups of 32-row waves fit one round of
+            // the resident workgroups (two per CU) and the work is causal or
+            // would still fit it at 16: twice the tile groups, and for causal
+            // work two laps that pair the triangle's long tile groups with its
+            // short ones (measured on MI355X: one 2048-token causal prompt,
+            // 32/8 heads, 74.7 -> 69.1 us)
+            const int64_t t2 = ceil_div(rows, 32);
+            const int64_t items2 = (int64_t)num_seqs * dims->num_kv_heads * t2;
+            const int32_t ns2 = prefill_nsplit(dims, prefill_bps(dims, blocks_per_split, items2, cus));
+            const int64_t need2 = ceil_div((int64_t)num_seqs * ns2 * dims->num_kv_heads, 8) * ceil_div(t2, 4);
+            const int64_t resident = (int64_t)(cus >= 8 ? cus / 8 : 1) * 2;   // workgroups per XCD
+            if (need2 <= resident && (causal || 2 * need2 <= resident)) rb = 1;
+        }
     }
     if (rb > max_rb) rb = max_rb;
     const int32_t ntiles = (int32_t)ceil_div((int64_t)q_len * G, 16 * rb);
-    const int cus = device_cus();
     const int64_t items = (int64_t)num_seqs * dims->num_kv_heads * ntiles;
     const int32_t bps = prefill_bps(dims, blocks_per_split, items, cus);
     const int32_t nsplit = prefill_nsplit(dims, bps);
