@@ -114,6 +114,9 @@ def test_state_and_workspace_sizes():
     assert pda.pda_workspace_bytes(d, 0) >= pda.pda_workspace_bytes(d, auto)
     big = dims(tile_capacity=4096)
     assert pda.pda_blocks_per_split(big, 0) >= 4096 // 256
+    # the library's split: about 256 tokens, 352 above head dim 128 (at most 256 splits)
+    for D, bs, want in ((128, 16, 16), (64, 8, 32), (256, 16, 22), (256, 32, 11), (200, 16, 22)):
+        assert pda.pda_blocks_per_split(dims(head_dim=D, block_size=bs, tile_capacity=512), 0) == want
     assert pda.pda_state_bytes(dims(num_q_heads=6, num_kv_heads=4)) == 0
 
 
