@@ -455,7 +455,14 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         x.ng = (x.t1 - x.t0 + 15) >> 4;
     };
 
+    // Items past the first wave's-worth come from the work counter; when
+    // there are no more items than waves, every wave's first item is its
+    // last and no claim is made (a claim is an atomic on one word: a
+    // thousand of them at once, as at the end of a one-round launch, queue
+    // for microseconds).
+    const bool claims = nitems > nwaves;
     auto claim_next = [&]() {
+        if (!claims) return nitems;
         const int grabbed = lane == 0 ? (int)epoch_claim(a.work, a.epoch) : 0;
         return nwaves + readlane(grabbed, 0);
     };
@@ -1037,8 +1044,9 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         int n = 0;
         for (int r = 0; r < (staged ? rA : nr - 1); ++r, n += NBUF) round(n);
         if (staged) {
-            claim_raw = lane == 0 ? __hip_atomic_fetch_add(a.work, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                  : 0ull;
+            claim_raw = !claims ? ((unsigned long long)a.epoch << 32) | (unsigned)(nitems - nwaves)
+                        : lane == 0 ? __hip_atomic_fetch_add(a.work, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0ull;
             round(n);
             n += NBUF;
             const uint32_t chi = (uint32_t)readlane((int)(uint32_t)(claim_raw >> 32), 0);
