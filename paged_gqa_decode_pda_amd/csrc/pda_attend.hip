@@ -203,7 +203,8 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int units = a.Hkv * a.nhc;
-    const int span = a.bps * a.bs;
+    // pages and tokens per split: the launch's, or longer ones chosen below
+    int bpsx = a.bps, span = a.bps * a.bs;
     const int qd = lane >> 4, col = lane & 15;
 
     // Restart the launch's counters at its epoch before anything claims on
@@ -239,7 +240,10 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         // items span kBigTokensLarge tokens and take kEighthsLarge / 8 of the
         // splits; with less, every split is an item as long as there are no
         // more split items than waves (one round, equal lengths), else
-        // kEighthsPaired / 8 of the splits go in pairs.
+        // longer splits (up to kWidenMax times the launch's) if some make no
+        // more items than waves, else
+        // kEighthsPaired / 8 of the splits go in pairs.  Splits only grow,
+        // so a sequence never has more items than partial slots.
         float tot = 0.f, nspl = 0.f;
         for (int s = tid; s < a.S; s += kMThreads) {
             const int nt = seq_tokens(a.counts, a.lastv, a.lv_default, s, a.cap, a.bs);
@@ -266,8 +270,21 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
             eighths = kEighthsLarge;
             sgl = kSinglesLarge;
         } else if (nspl * (float)units > waves) {
-            big = 2;
-            eighths = kEighthsPaired;
+            // A sequence of n tokens makes at most n / L + 1 items of L
+            // tokens (an empty one makes one), so L >= tot / (waves / units
+            // - S) makes no more items than waves; the fewest pages that
+            // reach that bound, if no more than kWidenMax times the launch's.
+            const float room = waves / (float)units - (float)a.S;
+            const float need = room >= 1.f ? ceilf(tot / (room * (float)a.bs)) : 3e9f;
+            if (need <= (float)(kWidenMax * a.bps)) {
+                bpsx = max(a.bps + 1, (int)need);
+                span = bpsx * a.bs;
+                big = 1;
+                eighths = 0;
+            } else {
+                big = 2;
+                eighths = kEighthsPaired;
+            }
         } else {
             big = 1;
             eighths = 0;
@@ -405,7 +422,7 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
         const int hc = unit - x.g * a.nhc;
         x.h0 = x.g * a.G + hc * HPI;
         x.nh = min(HPI, a.G - hc * HPI);
-        x.cb = x.split * a.bps;
+        x.cb = x.split * bpsx;
     };
 
     auto fetch = [&](MItem<DP> &x, int &cnt_raw, int &lv_raw) {

@@ -71,13 +71,19 @@ constexpr int kPrefixMaxSeqs = 10240;
 // per wave, "big" items span kBigTokensLarge tokens (at least one split) and
 // take kEighthsLarge / 8 of a sequence's splits; with less, every split is an
 // item of its own when that makes no more items than waves (one round, equal
-// lengths), else kEighthsPaired / 8 of the splits go in pairs (measured on
-// MI355X for batch 16, contexts 512-4096: 0, 2, 4, 6, 7, 8 eighths paired
-// gave 54.6, 51.6, 47.7, 44.4, 43.3, 43.7 us per step; fewer, longer items
-// keep HBM as busy and leave shorter merges).
+// lengths); failing that, splits of as many pages as a bound on the item
+// count says make no more items than waves, if that is at most kWidenMax
+// times the launch's pages per split; failing that too, kEighthsPaired / 8 of
+// the splits go in
+// pairs (measured on MI355X for batch 16, contexts 512-4096, 256-token
+// splits: 0, 2, 4, 6, 7, 8 eighths paired gave 54.6, 51.6, 47.7, 44.4, 43.3,
+// 43.7 us per step; fewer, longer items keep HBM as busy and leave shorter
+// merges; the same batch with one round of 304- to 416-token splits took
+// 35.2-36.8 us against 39.4 paired).
 constexpr int kBigTokensLarge = 1024;
 constexpr int kEighthsLarge = 7;
 constexpr int kEighthsPaired = 7;
+constexpr int kWidenMax = 2;
 // With at least kBigTokensLarge tokens of work per wave, the splits that a
 // sequence with big items has left go kSinglesLarge at a time (the last item
 // takes what remains): measured on MI355X, items of 512 tokens there beat 256

@@ -103,9 +103,9 @@ def build_case(rng: np.random.Generator, S, Hq, Hkv, D, bs, contexts, layout="pa
         Kc = np.full((P, bs, Hkv, D), poison, np.uint16)
         Vc = np.full((P, bs, Hkv, D), poison, np.uint16)
         for s in range(S):
-            for t in range(contexts[s]):
-                Kc[seq_pages[s][t // bs], t % bs] = to_bits(K[s][t])
-                Vc[seq_pages[s][t // bs], t % bs] = to_bits(V[s][t])
+            t = np.arange(contexts[s])
+            Kc[seq_pages[s][t // bs], t % bs] = to_bits(K[s])
+            Vc[seq_pages[s][t // bs], t % bs] = to_bits(V[s])
         pool = np.concatenate([Kc.ravel(), Vc.ravel()])
         st = [x // 2 for x in Kc.strides]
         strides = (st[0], st[1], st[2])
@@ -113,9 +113,10 @@ def build_case(rng: np.random.Generator, S, Hq, Hkv, D, bs, contexts, layout="pa
     elif layout == "scratch":
         X = np.full((P, 2, Hkv, bs, D), poison, np.uint16)
         for s in range(S):
-            for t in range(contexts[s]):
-                X[seq_pages[s][t // bs], 0, :, t % bs] = to_bits(K[s][t])
-                X[seq_pages[s][t // bs], 1, :, t % bs] = to_bits(V[s][t])
+            t = np.arange(contexts[s])
+            # advanced indices split by a slice: the token axis comes first
+            X[seq_pages[s][t // bs], 0, :, t % bs] = to_bits(K[s])
+            X[seq_pages[s][t // bs], 1, :, t % bs] = to_bits(V[s])
         pool = X.ravel().copy()
         st = [x // 2 for x in X.strides]
         strides = (st[0], st[3], st[2])

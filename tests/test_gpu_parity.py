@@ -305,6 +305,40 @@ def test_full_size_workloads_sampled(name):
     print(f"{name} sampled max/mean err {e}")
 
 
+@pytest.mark.parametrize("k,T", [(1, 1), (5, 1), (8, 1), (9, 1), (1, 2), (9, 2)])
+def test_split_widening_one_round(k, T):
+    """Small-work launches with more 256-token splits than waves.  The kernel
+    bounds the item count of a split length L by tot / L + S per kv-head unit
+    and takes the fewest pages that make that bound fit the waves, if that
+    is at most twice 16 pages (k 1 and 5 here: 21 and 30 pages); else it
+    pairs splits (k 8 and 9).  Every output row against the oracle, decode
+    and tiled (the tiled launch decides per tile; every tile here has the
+    same shape)."""
+    import torch
+    waves = 4 * torch.cuda.get_device_properties(0).multi_processor_count
+    S, Hq, Hkv, D, bs, bps = waves // 8, 4, 1, 128, 16, 16
+    span_k = 16 * (16 + 2 * k)
+    rng = np.random.Generator(np.random.PCG64(4200 + 10 * k + T))
+    short = rng.integers(0, 16, size=S)
+    short[0] = 0   # one sequence exactly at eight splits of span_k per tile
+    tile_tok = [np.full(S, 8 * span_k), 8 * span_k - short]   # a full tile's tokens, the last tile's
+    for tok in tile_tok:
+        assert int(np.sum(-(-tok // (bps * bs)))) > waves and int(tok.sum()) < 1024 * waves
+        need = int(np.ceil(tok.sum() / ((waves - S) * bs)))   # one kv-head unit
+        assert (need <= 2 * bps) == (k <= 5)
+        if need <= 2 * bps:   # the widened split makes one round of items
+            assert int(np.sum(-(-tok // (need * bs)))) <= waves
+    ctx = T * 8 * span_k - short   # tiles split the pages evenly: all full but the last
+    announce("split widening", "k", k, "S", S, "waves", waves, "tiles", T)
+    case = build_case(rng, S, Hq, Hkv, D, bs, ctx, layout="paged", n_tiles=T)
+    dev = Device(case)
+    ref = oracle_of(dev)
+    if T == 1:
+        assert_parity(out_to_f64(dev.decode()), ref["out"], label=f"decode widen {k}")
+    _, out = dev.tiled()
+    assert_parity(out_to_f64(out), ref["out"], label=f"tiled widen {k} tiles {T}")
+
+
 @pytest.mark.parametrize("S", [10240, 10241])
 def test_many_sequences_both_enumerations(S):
     """Up to 10240 sequences the decode kernel enumerates work items through a
