@@ -124,7 +124,9 @@ int32_t pda_blocks_per_split(const pda_dims *dims, int32_t blocks_per_split);
  * padded up to a multiple of 16, then the o rows, rows * slots * head_dim * 4,
  * where rows = max_seqs * num_q_heads and slots = ceil(tile_capacity / bps),
  * one per split (the kernel may group splits into larger work items, which
- * then share a slot).
+ * then share a slot, or, in a launch with too little work for more than one
+ * round of split items, lengthen every split up to twice bps pages: splits
+ * only grow, so a sequence never needs more slots than this).
  * The workspace needs no clearing, before its first use or ever: every
  * counter is tagged with the launch that counts in it, and a launch restarts
  * any counter another launch (or leftover content) left behind.  Calls that
