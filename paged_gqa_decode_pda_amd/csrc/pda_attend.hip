@@ -207,17 +207,6 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     int bpsx = a.bps, span = a.bps * a.bs;
     const int qd = lane >> 4, col = lane & 15;
 
-    // Restart the launch's counters at its epoch before anything claims on
-    // them, so that claims and arrival counts take the one-atomic path: the
-    // waves finishing their first items all at once would otherwise contend
-    // for the compare-and-swap that restarts a word found with another
-    // launch's epoch.
-    if (a.restart) {
-        const int64_t gsize = (int64_t)gridDim.x * kMThreads;
-        const int64_t gtid = (int64_t)blockIdx.x * kMThreads + tid;
-        if (gtid == 0) epoch_restart(a.work, a.epoch);
-        for (int64_t i = gtid; i < (int64_t)a.S * units; i += gsize) epoch_restart(a.arrive + i, a.epoch);
-    }
 
     // Work items.  With the prefix (up to kPrefixMaxSeqs sequences), each
     // sequence's splits are grouped: a share of them, `big` at a time, form
@@ -357,6 +346,21 @@ __global__ void __launch_bounds__(kMThreads) attend_kernel(const AttendArgs a) {
     __syncthreads();
 
     const int nwaves = (int)gridDim.x * kMWaves;
+    // A launch that makes claims restarts its counters at its epoch before
+    // its first items end, so that claims and arrival counts take the
+    // one-atomic path: the waves claiming after their first items would
+    // otherwise contend for the compare-and-swap that restarts a word found
+    // with another launch's epoch (measured: 7 % of a step on ragged batches).
+    // Without claims, the few arrivals on each word restart it themselves,
+    // and the pass's round trips are saved.  Either order of a restart and a
+    // claim or arrival on a word is correct (epoch_restart changes only a word
+    // of another epoch).
+    if (a.restart && nitems > nwaves) {
+        const int64_t gsize = (int64_t)gridDim.x * kMThreads;
+        const int64_t gtid = (int64_t)blockIdx.x * kMThreads + tid;
+        if (gtid == 0) epoch_restart(a.work, a.epoch);
+        for (int64_t i = gtid; i < (int64_t)a.S * units; i += gsize) epoch_restart(a.arrive + i, a.epoch);
+    }
     const int tok32 = (int)a.tok;
     const int32_t *lv_src = a.lastv ? a.lastv : a.counts;
 
