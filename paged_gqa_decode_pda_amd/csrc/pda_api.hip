@@ -221,9 +221,10 @@ pda::AttendArgs attend_args(const pda_dims *d, const void *q, const void *k, con
     a.lv_default = lv_default;
     a.prefix_mode = S <= pda::kPrefixMaxSeqs ? 1 : 0;
     a.epoch = next_epoch();
-    // Test knob: without the restart at the launch's start, every counter a
-    // launch finds with another epoch is restarted by its first claim (the
-    // claims' own path, otherwise taken only in a race with the restart).
+    // Test knob: without the restart pass of a launch that makes claims,
+    // every counter the launch finds with another epoch is restarted by its
+    // first claim or arrival (the path that launches without claims always
+    // take for arrivals, and claims only in a race with the pass).
     a.restart = std::getenv("PDA_DEBUG_NO_COUNTER_RESTART") ? 0 : 1;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d->head_dim));
     char *wsb = static_cast<char *>(ws);

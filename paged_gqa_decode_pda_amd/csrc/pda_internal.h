@@ -43,8 +43,9 @@ struct AttendArgs {
     int32_t S, Hq, Hkv, G, D, bs, cap, bps, nhc, nsplit, lv_default;
     int32_t prefix_mode;      // 1: enumerate only non-empty splits (needs 2 (S + 1) ints of LDS)
     uint32_t epoch;           // this launch's counter epoch (never reused by a recent launch)
-    int32_t restart;          // 1: restart the counters at the launch's start (0 only to test the
-                              // claims' own restart: PDA_DEBUG_NO_COUNTER_RESTART set)
+    int32_t restart;          // 1: a launch that makes claims restarts the counters after its
+                              // enumeration (0 only to test the claims' own restart:
+                              // PDA_DEBUG_NO_COUNTER_RESTART set)
     float scale_log2;         // log2(e) / sqrt(D)
 };
 
